@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs shared by the CPU oracle and the HIP path.
+
+This module only *draws* inputs. It holds none of the attention arithmetic:
+no scores, no softmax, no products. Both sides of every parity check take
+their inputs from here, so they see bit-identical values.
+
+Recipe (the pages give no generator, so this is a stated choice):
+
+* ``numpy.random.default_rng(seed)``; ``standard_normal(dtype=float32)``
+  drawn in the order Q, K, V, dO, each of shape [B, H, N, d]
+  (the [N, d]-per-head layout of the tutorial page "Flash Attention —
+  Revolutionizing Transformer Efficiency Through Memory-Aware Algorithms",
+  section "The Memory Wall Problem").
+* bf16 inputs are the fp32 draws rounded to nearest, ties to even, on the
+  fp32 bit pattern. The fp32 value of those bf16 bits is what the oracle
+  receives, so both sides see the same numbers.
+* The block-sparse mask (the review page "FlashAttention: exact attention
+  made fast by counting memory traffic", section "The method", extension to
+  block-sparse attention) is one uint8 matrix of 128 x 128 blocks shared by
+  every (batch, head): diagonal blocks always kept, every off-diagonal block
+  kept independently with probability 0.25, drawn from
+  ``default_rng(100 + seed).random((nb, nb)) < 0.25``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+MASK_NONE = 0
+MASK_CAUSAL = 1
+MASK_BLOCK_SPARSE = 2
+MASK_BLOCK = 128          # granularity of the block-sparse mask, in rows/cols
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention workload: shape, dtype, mask kind and seed."""
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: int          # DTYPE_BF16 or DTYPE_F32
+    mask_kind: int      # MASK_NONE / MASK_CAUSAL / MASK_BLOCK_SPARSE
+    backward: bool      # whether the workload includes the backward pass
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# The five workloads the build is measured and checked on.
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", 1, 1, 128, 64, DTYPE_F32, MASK_NONE, True, 1),
+    "gpt2_medium": Workload("gpt2_medium", 64, 16, 1024, 64, DTYPE_BF16, MASK_NONE, True, 2),
+    "causal_train": Workload("causal_train", 8, 16, 4096, 128, DTYPE_BF16, MASK_CAUSAL, True, 3),
+    "long_prefill": Workload("long_prefill", 1, 32, 32768, 128, DTYPE_BF16, MASK_CAUSAL, False, 4),
+    "block_sparse": Workload("block_sparse", 16, 16, 4096, 64, DTYPE_BF16, MASK_BLOCK_SPARSE, True, 5),
+}
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even.
+
+    NaN stays NaN (quiet), +-inf and values that round past the largest
+    finite bf16 become +-inf, subnormals round like any other value.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+    nan = np.isnan(x)
+    if nan.any():
+        r = np.where(nan, ((u >> 16) | 0x40).astype(np.uint32), r)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> their exact fp32 values."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_tensors(seed: int, shape, count: int) -> list[np.ndarray]:
+    """``count`` fp32 N(0,1) arrays of ``shape`` drawn in order from ``seed``."""
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal(shape, dtype=np.float32) for _ in range(count)]
+
+
+def block_mask(N: int, seed: int, p: float = 0.25, block: int = MASK_BLOCK) -> np.ndarray:
+    """uint8 [nb, nb] keep-mask, nb = ceil(N / block); diagonal forced to 1."""
+    nb = -(-N // block)
+    rng = np.random.default_rng(100 + seed)
+    m = (rng.random((nb, nb)) < p).astype(np.uint8)
+    np.fill_diagonal(m, 1)
+    return m
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Inputs of one workload.
+
+    ``q, k, v, do`` are fp32 arrays holding exactly the values the GPU sees
+    (for bf16 they are the bf16-rounded draws). ``*_bits`` are the uint16
+    bf16 patterns (None for fp32 workloads). ``mask`` is the uint8 block mask
+    or None.
+    """
+    w: Workload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray | None
+    q_bits: np.ndarray | None = None
+    k_bits: np.ndarray | None = None
+    v_bits: np.ndarray | None = None
+    do_bits: np.ndarray | None = None
+    mask: np.ndarray | None = None
+
+
+def make_inputs(w: Workload, seed: int | None = None, with_do: bool | None = None) -> Inputs:
+    """Draw the inputs of workload ``w`` (seed defaults to ``w.seed``)."""
+    seed = w.seed if seed is None else seed
+    with_do = w.backward if with_do is None else with_do
+    shape = (w.B, w.H, w.N, w.d)
+    arrs = normal_tensors(seed, shape, 4 if with_do else 3)
+    mask = block_mask(w.N, seed) if w.mask_kind == MASK_BLOCK_SPARSE else None
+    if w.dtype == DTYPE_F32:
+        q, k, v = arrs[:3]
+        do = arrs[3] if with_do else None
+        return Inputs(w, q, k, v, do, mask=mask)
+    bits = [bf16_bits(a) for a in arrs]
+    del arrs
+    vals = [bf16_to_f32(b) for b in bits]
+    return Inputs(w, vals[0], vals[1], vals[2], vals[3] if with_do else None,
+                  bits[0], bits[1], bits[2], bits[3] if with_do else None, mask=mask)
+
+
+def small_workload(B, H, N, d, dtype=DTYPE_BF16, mask_kind=MASK_NONE, seed=0, backward=True):
+    """A workload of arbitrary shape for parity cases (ragged N, tiny B, H)."""
+    return Workload(f"B{B}H{H}N{N}d{d}", B, H, N, d, dtype, mask_kind, backward, seed)
