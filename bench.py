@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+fa_fwd (O and LSE) followed by fa_bwd (row term, dK/dV, dQ), through the C
+ABI. The default workload is the GPT-2-medium attention shape (B=64, H=16,
+N=1024, d=64, bf16, no mask). Inputs are resident in device memory before the
+timed region starts.
+
+Prints ONE JSON line (rank 0) with the metric in TFLOP/s under the FLOP
+convention fwd = 4*d*vis, bwd = 10*d*vis per head (vis = visible
+query/key pairs), plus:
+  roofline      the forward kernel's achieved TFLOP/s (algorithmic FLOPs per
+                launch / its mean duration from HIP events on the launch
+                stream) against the MI355X dense bf16 MFMA peak;
+  cpu_baseline  the float64 CPU oracle timed on a bounded sample of the same
+                workload on this host's cores;
+  naive         the materialise-S torch composition (matmul, mask, softmax,
+                matmul, autograd) on the same inputs, for comparison.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 2516.6: 256 CUs x 2.4 GHz x 4096 FLOP/clk
+PEAK_F32_VALU_TFLOPS = 157.3
+A100_FIG2_MS = 7.3                                # the pages' GPT-2-medium attention runtime (context)
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def visible_pairs(w: synth.Workload, mask: np.ndarray | None) -> int:
+    """Visible (query, key) pairs per head."""
+    N = w.N
+    if w.mask_kind == synth.MASK_NONE:
+        return N * N
+    if w.mask_kind == synth.MASK_CAUSAL:
+        return N * (N + 1) // 2
+    nb = mask.shape[0]
+    sizes = np.array([min(128, N - 128 * i) for i in range(nb)], dtype=np.int64)
+    return int((mask.astype(np.int64) * np.outer(sizes, sizes)).sum())
+
+
+def source_digest(*files: str) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(inp: synth.Inputs, budget_s: float, backward: bool, flop_per_head: float) -> dict:
+    """Times the float64 oracle (as it stands) on whole heads until ~budget_s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    w = inp.w
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rows = None
+    if w.N > 8192:          # a slice of rows of one head keeps the sample bounded
+        rows = np.arange(2048)
+    done = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        oracle.forward_head(inp.q[b, h], inp.k[b, h], inp.v[b, h], w.scale, w.mask_kind, inp.mask, rows)
+        if backward:
+            oracle.backward_head(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.do[b, h], w.scale, w.mask_kind, inp.mask)
+        done += 1
+        if rows is None:
+            flops += flop_per_head
+        else:
+            flops += flop_per_head * (rows.size / w.N) * (1.0 if w.mask_kind == synth.MASK_NONE else rows.size / w.N)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    what = "fwd+bwd" if backward else "fwd"
+    sample = f"{done} of {len(heads)} heads, {what}" + (f", query rows 0..{rows.size - 1}" if rows is not None else "")
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds": round(el, 2)}
+
+
+def naive_step(q, k, v, do, scale, mask_kind, bool_mask, backward):
+    """Materialise-S comparator: S and P go through device memory."""
+    import torch
+    qq = q.detach().requires_grad_(backward)
+    kk = k.detach().requires_grad_(backward)
+    vv = v.detach().requires_grad_(backward)
+    s = torch.matmul(qq, kk.transpose(-1, -2).contiguous()) * scale
+    if bool_mask is not None:
+        s = s.masked_fill(~bool_mask, float("-inf"))
+    p = torch.softmax(s.float(), dim=-1).to(q.dtype)
+    o = torch.matmul(p, vv)
+    if backward:
+        o.backward(do)
+    return o
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_medium", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-naive", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads are independent; sharding them needs no communication). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import io_aware_exact_10_amd as fa
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    backward = w.backward
+    print(f"# workload {w.name}: B{w.B} H{w.H} N{w.N} d{w.d} dtype{w.dtype} mask{w.mask_kind} "
+          f"{'fwd+bwd' if backward else 'fwd'}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w)
+
+    def dev_t(vals, bits):
+        if w.dtype == synth.DTYPE_BF16:
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(vals).to(dev)
+
+    q, k, v = dev_t(inp.q, inp.q_bits), dev_t(inp.k, inp.k_bits), dev_t(inp.v, inp.v_bits)
+    do = dev_t(inp.do, inp.do_bits) if backward else None
+    mask_t = torch.from_numpy(inp.mask).to(dev) if inp.mask is not None else None
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    if backward:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.forward(q, k, v, w.scale, w.mask_kind, mask_t, out=o, lse=lse)
+        if backward:
+            fa.backward(q, k, v, o, lse, do, w.scale, w.mask_kind, mask_t, workspace=ws, dq=dq, dk=dk, dv=dv)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fa.forward(q, k, v, w.scale, w.mask_kind, mask_t, out=o, lse=lse)
+        ev[i][1].record(stream)
+        if backward:
+            fa.backward(q, k, v, o, lse, do, w.scale, w.mask_kind, mask_t, workspace=ws, dq=dq, dk=dk, dv=dv)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])
+    bwd_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)])
+    step_ms = fwd_ms + bwd_ms
+    print(f"# timed {args.steps} steps: {step_ms.mean():.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
+          file=sys.stderr, flush=True)
+
+    vis = visible_pairs(w, inp.mask)
+    heads = w.B * w.H
+    fwd_flop = 4.0 * w.d * vis * heads
+    bwd_flop = 10.0 * w.d * vis * heads if backward else 0.0
+    ms_per_step = float(step_ms.mean())
+    value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = fwd_flop / (fwd_ms.mean() * 1e-3) / 1e12
+    bwd_tflops = bwd_flop / (bwd_ms.mean() * 1e-3) / 1e12 if backward else None
+
+    peak = PEAK_BF16_TFLOPS if w.dtype == synth.DTYPE_BF16 else PEAK_F32_VALU_TFLOPS
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        rec = json.load(open(PROFILE_TRAFFIC)).get(w.name, {}).get("fwd")
+        digest = source_digest("io_aware_exact_10_amd/csrc/fa_fwd_bf16.hip", "io_aware_exact_10_amd/csrc/fa_common.h")
+        if rec and rec.get("source_digest") == digest:
+            traffic = rec.get("hbm_bytes_per_launch")
+    roofline = {"kernel": "fwd_bf16_kernel" if w.dtype == synth.DTYPE_BF16 else "fwd_f32_kernel",
+                "bound": "mfma" if w.dtype == synth.DTYPE_BF16 else "alu",
+                "achieved": round(fwd_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                "frac": round(fwd_tflops / peak, 4), "traffic": traffic,
+                "flop_per_launch": fwd_flop, "mean_launch_ms": round(float(fwd_ms.mean()), 4)}
+
+    naive = None
+    if not args.no_naive and w.N <= 4096:
+        try:
+            bm = None
+            if w.mask_kind == synth.MASK_CAUSAL:
+                bm = torch.ones(w.N, w.N, dtype=torch.bool, device=dev).tril()
+            elif w.mask_kind == synth.MASK_BLOCK_SPARSE:
+                bm = mask_t.bool().repeat_interleave(128, 0).repeat_interleave(128, 1)[: w.N, : w.N]
+            for _ in range(2):
+                naive_step(q, k, v, do, w.scale, w.mask_kind, bm, backward)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 3
+            e0.record(stream)
+            for _ in range(reps):
+                naive_step(q, k, v, do, w.scale, w.mask_kind, bm, backward)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            nms = e0.elapsed_time(e1) / reps
+            naive = {"ms_per_step": round(nms, 3), "tflops": round((fwd_flop + bwd_flop) / (nms * 1e-3) / 1e12, 2),
+                     "what": "torch matmul, mask, softmax (fp32), matmul; autograd backward"}
+        except Exception as ex:  # noqa: BLE001
+            naive = {"error": repr(ex)[:200]}
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle sample", file=sys.stderr, flush=True)
+        flop_head = (fwd_flop + bwd_flop) / heads
+        cpu = cpu_baseline(inp, args.cpu_budget, backward, flop_head)
+
+    what = "fwd+bwd" if backward else "fwd"
+    mask_name = {0: "none", 1: "causal", 2: "block-sparse"}[w.mask_kind]
+    rec = {
+        "metric": "attention fwd / fwd+bwd TFLOP/s and % of bf16 MFMA peak, N=1k-32k, d=64/128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(A100_FIG2_MS / ms_per_step, 3) if w.name == "gpt2_medium" else None,
+        "dtype": "bf16" if w.dtype == synth.DTYPE_BF16 else "f32",
+        "data": "synthetic: Q, K, V, dO ~ N(0,1) seeded, bf16 round-to-nearest-even",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} mask={mask_name} {what}",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": mask_name, "pass": what,
+                   "seed": w.seed, "scale": w.scale},
+        "frac_of_peak": round(value / peak, 4),
+        "fwd": {"ms": round(float(fwd_ms.mean()), 4), "tflops": round(fwd_tflops, 2),
+                "frac": round(fwd_tflops / peak, 4), "gflop": round(fwd_flop / 1e9, 2)},
+        "bwd": ({"ms": round(float(bwd_ms.mean()), 4), "tflops": round(bwd_tflops, 2),
+                 "frac": round(bwd_tflops / peak, 4), "gflop": round(bwd_flop / 1e9, 2)} if backward else None),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "naive": naive,
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

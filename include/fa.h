@@ -1,0 +1,124 @@
+/*
+ * fa.h — C ABI of the gfx950 (MI355X) exact tiled attention library, libfa.so.
+ *
+ * The library computes exact softmax attention
+ *
+ *     O = softmax(scale * Q K^T  [+ causal or block-sparse mask]) V
+ *
+ * tile by tile with the online softmax, so the N x N score matrix never
+ * reaches device memory. The forward pass writes only O and the per-row
+ * log-sum-exp; the backward pass recomputes the probabilities block by block
+ * from Q, K, V and that log-sum-exp.
+ *
+ * Passages that define the operations (page title, then section):
+ *   - "FlashAttention: exact attention made fast by counting memory traffic",
+ *     "The method": tiling with running row statistics, exact result,
+ *     backward by recomputation from the output and the statistics, and the
+ *     block-sparse extension.
+ *   - "FlashAttention and IO-aware exact attention", "Core ideas": online
+ *     softmax, tiling and fusion with one log-sum-exp kept per row, backward
+ *     by recomputation; "How to approach it": causal masking.
+ *   - "Flash Attention — Revolutionizing Transformer Efficiency Through
+ *     Memory-Aware Algorithms", "The Memory Wall Problem" ([N, d] operands,
+ *     S = QK^T, softmax, O = PV) and "Online Softmax Algorithm".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory. Every tensor pointer is DEVICE memory owned by the caller; the
+ *   library never allocates, frees or keeps a pointer after a call returns.
+ * Layout. q, k, v, o, dO, dq, dk, dv are contiguous [B, H, N, d] row-major
+ *   arrays (d fastest), in the element type `dtype` (FA_BF16: bfloat16 bits;
+ *   FA_F32: IEEE float). lse and the backward's row term are float [B, H, N].
+ * lse. Natural log of sum_j exp(scale * q_i . k_j) over the keys j visible to
+ *   query i; -inf for a row with no visible key (its O row is 0).
+ * Masks. FA_MASK_NONE: every key visible. FA_MASK_CAUSAL: key j visible to
+ *   query i iff j <= i (query and key sequences both have length N).
+ *   FA_MASK_BLOCK_SPARSE: block_mask is a device uint8 array of
+ *   ceil(N/128) x ceil(N/128) entries, row-major (query block, key block),
+ *   nonzero = keep; one mask is shared by every (batch, head); the masks are
+ *   not combined. block_mask is read only for FA_MASK_BLOCK_SPARSE and may
+ *   be NULL otherwise. The library never reads mask contents on the host.
+ * Supported. d in {64, 128}; dtype FA_BF16 (bf16 in and out, fp32
+ *   accumulation, probabilities rounded to bf16 before the P.V product) or
+ *   FA_F32 (fp32 throughout). Any finite scale, including negative and 0.
+ * Errors. Arguments are validated on the host before anything is enqueued;
+ *   on any error a negative fa_status is returned and no output is touched.
+ *   Tensor pointers must be 16-byte aligned, lse 4-byte aligned. Outputs must
+ *   not overlap inputs or each other. FA_OK means the work was enqueued on
+ *   `stream` (asynchronous); FA_ERR_HIP means a launch failed (the HIP error
+ *   is not cleared). A device fault surfaces at the caller's next
+ *   synchronisation.
+ * State. No global mutable state; calls are thread-safe. Results are
+ *   bitwise deterministic from run to run (no atomics).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,       /* B, H or N < 1, or the element count overflows */
+  FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}, or an unknown dtype */
+  FA_ERR_MASK = -4,        /* unknown mask_kind, or block_mask NULL for a block-sparse call */
+  FA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
+  FA_ERR_ALIGN = -6,       /* a pointer is not aligned as stated above */
+  FA_ERR_HIP = -7,         /* a kernel launch returned a HIP error */
+  FA_ERR_ARG = -8          /* non-finite scale, or an output overlaps another tensor */
+} fa_status;
+
+typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_BLOCK_SPARSE = 2 } fa_mask_kind;
+typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
+
+/*
+ * Forward pass. Reads q, k, v [B,H,N,d]; writes o [B,H,N,d] and lse [B,H,N].
+ * Each workgroup keeps one tile of queries resident and streams the visible
+ * key/value tiles through on-chip memory with the online softmax ("The
+ * method"; "Core ideas": online softmax, tiling and fusion).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale,
+           int mask_kind, const uint8_t* block_mask, int dtype, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: the float row term
+ * D_i = sum_k dO_ik O_ik for every (b, h, i), rounded up to 256 bytes.
+ * Returns 0 if the shape is invalid.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass. Reads q, k, v, o, lse (as written by fa_fwd with the same
+ * arguments) and dO; writes dq, dk, dv [B,H,N,d]. Probabilities are
+ * recomputed tile by tile from q, k and lse ("The method": backward by
+ * recomputation; "Core ideas": backward by recomputation). The gradient
+ * formulas are the derivative of the forward definition:
+ *   dV = P^T dO; dP = dO V^T; D = rowsum(dO * O); dS = P * (dP - D);
+ *   dQ = scale dS K; dK = scale dS^T Q.
+ * Three kernels run in order on `stream`: the row term, then dK/dV (one
+ * workgroup per key tile), then dQ (one workgroup per query tile).
+ * workspace: caller-owned device memory of at least
+ * fa_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte aligned; its contents
+ * on entry are ignored and on exit are unspecified.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale,
+           int mask_kind, const uint8_t* block_mask, int dtype,
+           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static, human-readable name of a fa_status value ("unknown status" otherwise). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,188 @@
+"""Python binding of libfa.so, the gfx950 exact tiled attention library.
+
+Argument marshalling only: every step of the attention computation runs in
+the HIP kernels behind the C ABI declared in ``include/fa.h``. PyTorch
+supplies device memory and the current stream; nothing here computes.
+
+Low-level calls mirror the C ABI names (``fa_fwd``, ``fa_bwd``,
+``fa_bwd_workspace_bytes``, ``fa_status_string``) and take raw integer
+device pointers. ``forward`` / ``backward`` are conveniences that take torch
+tensors of shape [B, H, N, d] and allocate the outputs.
+
+There is no fallback: if ``libfa.so`` has not been built, importing this
+module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch  # loads the HIP runtime first, so libfa.so binds to the same one
+
+__all__ = [
+    "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_MASK",
+    "FA_ERR_WORKSPACE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_ARG",
+    "MASK_NONE", "MASK_CAUSAL", "MASK_BLOCK_SPARSE", "DTYPE_BF16", "DTYPE_F32",
+    "FAError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string",
+    "forward", "backward", "library_path", "lib",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "fa.h")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
+FA_ERR_MASK, FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_ARG = -4, -5, -6, -7, -8
+MASK_NONE, MASK_CAUSAL, MASK_BLOCK_SPARSE = 0, 1, 2
+DTYPE_BF16, DTYPE_F32 = 0, 1
+MASK_BLOCK = 128
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A libfa call returned a negative status."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {fa_status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfa.so (loaded on first use; raises if not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m io_aware_exact_10_amd.build` "
+                "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
+        L.fa_fwd.restype = i
+        L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+        L.fa_bwd.restype = i
+        L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        L.fa_bwd_workspace_bytes.restype = sz
+        L.fa_status_string.argtypes = [i]
+        L.fa_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/fa.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", txt)))
+
+
+# ---------------------------------------------------------------------------
+# C ABI mirrors (raw pointers as Python ints)
+# ---------------------------------------------------------------------------
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, block_mask, dtype, stream) -> int:
+    return int(lib().fa_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), mask_kind,
+                            block_mask, dtype, stream))
+
+
+def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, mask_kind, block_mask, dtype,
+           workspace, workspace_bytes, stream) -> int:
+    return int(lib().fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, ctypes.c_float(scale),
+                            mask_kind, block_mask, dtype, workspace, workspace_bytes, stream))
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences
+# ---------------------------------------------------------------------------
+_DT = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}
+
+
+def _check_qkv(q, k, v):
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have the same shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT:
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    for t in (q, k, v):
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _mask_ptr(mask_kind, block_mask, N, device):
+    if mask_kind != MASK_BLOCK_SPARSE:
+        return None
+    if block_mask is None:
+        raise ValueError("block_mask is required for MASK_BLOCK_SPARSE")
+    nb = -(-N // MASK_BLOCK)
+    if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != (nb, nb):
+        raise ValueError(f"block_mask must be uint8 [{nb}, {nb}]")
+    if not block_mask.is_cuda or not block_mask.is_contiguous() or block_mask.device != device:
+        raise ValueError("block_mask must be a contiguous tensor on the same GPU")
+    return block_mask.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def forward(q, k, v, scale=None, mask_kind=MASK_NONE, block_mask=None, out=None, lse=None):
+    """Attention forward on the current stream; returns (o, lse).
+
+    q, k, v: contiguous [B, H, N, d] bf16 or fp32 GPU tensors; scale defaults
+    to 1/sqrt(d). lse is fp32 [B, H, N] (natural log).
+    """
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    mp = _mask_ptr(mask_kind, block_mask, N, q.device)
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                B, H, N, d, scale, mask_kind, mp, _DT[q.dtype], _stream(q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return o, lse
+
+
+def backward(q, k, v, o, lse, do, scale=None, mask_kind=MASK_NONE, block_mask=None,
+             workspace=None, dq=None, dk=None, dv=None):
+    """Attention backward on the current stream; returns (dq, dk, dv)."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    for t in (o, do):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("o and do must match q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    mp = _mask_ptr(mask_kind, block_mask, N, q.device)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, mask_kind, mp,
+                _DT[q.dtype], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                _stream(q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

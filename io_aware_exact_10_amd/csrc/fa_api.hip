@@ -1,0 +1,147 @@
+// C ABI of libfa.so: host-side argument validation and kernel dispatch.
+// Every check runs before anything is enqueued, so an invalid call returns a
+// negative status and leaves all outputs untouched. No HIP API is called on
+// an error path. The declarations and their contract live in include/fa.h.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;   // per tensor; offsets are 64-bit inside
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap?
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int check_common(int B, int H, int N, int d, float scale, int mask_kind, const uint8_t* block_mask,
+                 int dtype, int64_t* elems) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  const int64_t e = (int64_t)B * H * N;
+  if (e > kMaxElems / 128) return FA_ERR_SHAPE;
+  if ((int64_t)B * H * (((int64_t)N + 63) / 64) >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_ERR_ARG;
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL && mask_kind != FA_MASK_BLOCK_SPARSE)
+    return FA_ERR_MASK;
+  if (mask_kind == FA_MASK_BLOCK_SPARSE && block_mask == nullptr) return FA_ERR_MASK;
+  *elems = e * d;
+  return FA_OK;
+}
+
+fa::AttnParams make_params(int B, int H, int N, int d, float scale, int mask_kind,
+                           const uint8_t* block_mask) {
+  fa::AttnParams p = {};
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.nblk = (N + 127) / 128;
+  p.scale = scale;
+  p.c = fabsf(scale) * 1.4426950408889634f;
+  p.qflip = scale < 0.f ? 0x80008000u : 0u;
+  p.block_mask = mask_kind == FA_MASK_BLOCK_SPARSE ? block_mask : nullptr;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and the sizes must fit)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype (d must be 64 or 128; dtype bf16 or f32)";
+    case FA_ERR_MASK: return "invalid mask (unknown mask_kind, or block_mask NULL for block-sparse)";
+    case FA_ERR_WORKSPACE: return "workspace NULL or smaller than fa_bwd_workspace_bytes()";
+    case FA_ERR_ALIGN: return "misaligned pointer (tensors 16-byte, lse 4-byte aligned)";
+    case FA_ERR_HIP: return "HIP kernel launch failed";
+    case FA_ERR_ARG: return "invalid argument (non-finite scale or overlapping output)";
+    default: return "unknown status";
+  }
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  const size_t rows = (size_t)B * (size_t)H * (size_t)N;
+  return (rows * sizeof(float) + 255) & ~(size_t)255;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale,
+           int mask_kind, const uint8_t* block_mask, int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int64_t elems = 0;
+  int st = check_common(B, H, N, d, scale, mask_kind, block_mask, dtype, &elems);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  const size_t tb = (size_t)elems * (dtype == FA_BF16 ? 2 : 4);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) || overlap(o, tb, lse, lb) ||
+      overlap(lse, lb, q, tb) || overlap(lse, lb, k, tb) || overlap(lse, lb, v, tb))
+    return FA_ERR_ARG;
+  fa::AttnParams p = make_params(B, H, N, d, scale, mask_kind, block_mask);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  const int e = dtype == FA_BF16 ? fa::launch_fwd_bf16(p, mask_kind, stream)
+                                 : fa::launch_fwd_f32(p, mask_kind, stream);
+  return e == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale,
+           int mask_kind, const uint8_t* block_mask, int dtype,
+           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
+  int64_t elems = 0;
+  int st = check_common(B, H, N, d, scale, mask_kind, block_mask, dtype, &elems);
+  if (st != FA_OK) return st;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
+  const size_t tb = (size_t)elems * (dtype == FA_BF16 ? 2 : 4);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const void* ins[6] = {q, k, v, o, dO, lse};
+  const size_t insz[6] = {tb, tb, tb, tb, tb, lb};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const size_t outsz[4] = {tb, tb, tb, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ARG;
+  }
+  fa::AttnParams p = make_params(B, H, N, d, scale, mask_kind, block_mask);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = const_cast<void*>(o);
+  p.lse = const_cast<float*>(lse);
+  p.dO = dO;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dterm = (float*)workspace;
+  const int e = dtype == FA_BF16 ? fa::launch_bwd_bf16(p, mask_kind, stream)
+                                 : fa::launch_bwd_f32(p, mask_kind, stream);
+  return e == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

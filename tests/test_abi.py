@@ -1,0 +1,144 @@
+"""The C-ABI library loads, exports what include/fa.h declares, and rejects
+invalid arguments with the documented status before touching the GPU.
+
+CPU only: every call below fails host-side validation, which runs before any
+HIP API call, so no device is needed (pointers are fake, never dereferenced).
+"""
+import math
+import os
+
+import pytest
+
+import io_aware_exact_10_amd as fa
+
+A = 0x10000          # fake, 16-byte aligned "device" addresses
+BIG = 1 << 30        # spacing so fake tensors never overlap
+
+
+def ptrs(n):
+    return [A + i * BIG for i in range(n)]
+
+
+def fwd_args(**kw):
+    q, k, v, o, lse = ptrs(5)
+    args = dict(q=q, k=k, v=v, o=o, lse=lse, B=1, H=2, N=256, d=64, scale=0.125,
+                mask_kind=fa.MASK_NONE, block_mask=None, dtype=fa.DTYPE_BF16, stream=None)
+    args.update(kw)
+    return args
+
+
+def bwd_args(**kw):
+    q, k, v, o, lse, do, dq, dk, dv, ws = ptrs(10)
+    args = dict(q=q, k=k, v=v, o=o, lse=lse, dO=do, dq=dq, dk=dk, dv=dv, B=1, H=2, N=256, d=64,
+                scale=0.125, mask_kind=fa.MASK_NONE, block_mask=None, dtype=fa.DTYPE_BF16,
+                workspace=ws, workspace_bytes=fa.fa_bwd_workspace_bytes(1, 2, 256, 64), stream=None)
+    args.update(kw)
+    return args
+
+
+def call_fwd(**kw):
+    return fa.fa_fwd(**fwd_args(**kw))
+
+
+def call_bwd(**kw):
+    return fa.fa_bwd(**bwd_args(**kw))
+
+
+def test_library_exports_every_declared_symbol():
+    names = fa.declared_functions()
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string"}
+    L = fa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_single_hip_runtime_in_process():
+    """libfa.so must bind to the HIP runtime torch already loaded."""
+    fa.lib()
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(hip) == 1, hip
+
+
+def test_status_strings():
+    codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_MASK,
+             fa.FA_ERR_WORKSPACE, fa.FA_ERR_ALIGN, fa.FA_ERR_HIP, fa.FA_ERR_ARG]
+    seen = set()
+    for c in codes:
+        s = fa.fa_status_string(c)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == len(codes)
+    assert fa.fa_status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 64) == 256
+    assert fa.fa_bwd_workspace_bytes(2, 3, 1000, 128) == ((2 * 3 * 1000 * 4 + 255) // 256) * 256
+    assert fa.fa_bwd_workspace_bytes(64, 16, 1024, 64) == 64 * 16 * 1024 * 4
+    for bad in ((0, 1, 1, 64), (1, 0, 1, 64), (1, 1, 0, 64), (1, 1, 8, 96)):
+        assert fa.fa_bwd_workspace_bytes(*bad) == 0
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse"])
+def test_fwd_null(name):
+    assert call_fwd(**{name: None}) == fa.FA_ERR_NULL
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse", "dO", "dq", "dk", "dv"])
+def test_bwd_null(name):
+    assert call_bwd(**{name: None}) == fa.FA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=-1), fa.FA_ERR_SHAPE), (dict(N=0), fa.FA_ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 20, N=1 << 10), fa.FA_ERR_SHAPE),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask_kind=3), fa.FA_ERR_MASK), (dict(mask_kind=-1), fa.FA_ERR_MASK),
+    (dict(mask_kind=2, block_mask=None), fa.FA_ERR_MASK),
+    (dict(scale=math.nan), fa.FA_ERR_ARG), (dict(scale=math.inf), fa.FA_ERR_ARG),
+    (dict(q=A + 8), fa.FA_ERR_ALIGN), (dict(o=3 * BIG + A + 2), fa.FA_ERR_ALIGN),
+    (dict(lse=4 * BIG + A + 2), fa.FA_ERR_ALIGN),
+    (dict(o=A), fa.FA_ERR_ARG),                      # o aliases q
+    (dict(lse=A + 64), fa.FA_ERR_ARG),               # lse inside q
+])
+def test_fwd_validation(kw, code):
+    assert call_fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(workspace=None), fa.FA_ERR_WORKSPACE),
+    (dict(workspace_bytes=16), fa.FA_ERR_WORKSPACE),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask_kind=2, block_mask=None), fa.FA_ERR_MASK),
+    (dict(scale=-math.inf), fa.FA_ERR_ARG),
+    (dict(dq=6 * BIG + A + 4), fa.FA_ERR_ALIGN),
+    (dict(workspace=9 * BIG + A + 8), fa.FA_ERR_ALIGN),
+    (dict(dk=A + 2 * BIG), fa.FA_ERR_ARG),           # dk aliases v
+    (dict(dv=6 * BIG + A), fa.FA_ERR_ARG),           # dv aliases dq
+    (dict(workspace=8 * BIG + A + 128), fa.FA_ERR_ARG),  # workspace inside dv
+])
+def test_bwd_validation(kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_torch_wrappers_reject_bad_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)                           # CPU tensors
+    with pytest.raises(ValueError):
+        fa.forward(q[0], q[0], q[0])                  # wrong rank
+    with pytest.raises(ValueError):
+        fa.forward(q, q.float(), q)                   # mixed dtypes
+
+
+def test_product_path_does_not_reference_the_oracle():
+    """The package source must not import or call the CPU oracle."""
+    pkg = os.path.dirname(fa.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(root, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
