@@ -17,6 +17,10 @@
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -53,6 +57,84 @@ __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum of the two bf16 halves of a packed pair, accumulated into c (fp32).
+__device__ __forceinline__ float dot2_ones(uint32_t pair, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                        __builtin_bit_cast(bf16x2, 0x3f803f80u), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles: dense row-major [rows][D] bf16, 16-byte chunk c of row r stored
+// at chunk position c ^ swz<D>(r). The swizzle keeps two access patterns
+// free of bank conflicts on the 64-bank LDS: 16-byte reads of one chunk from
+// 16 consecutive rows (MFMA operands taken along a row), and 8-byte
+// transpose reads (ds_read_b64_tr_b16) of 4 consecutive rows x 64 bytes
+// (MFMA operands taken down a column).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "head dim");
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+// Byte offset of element (r, col) of a swizzled tile; col is a multiple of 4.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  return r * (D * 2) + ((((col >> 3) ^ swz<D>(r))) << 4) + ((col & 7) << 1);
+}
+
+// Asynchronous copy of rows [r0, r0 + ROWS) of a [N, D] bf16 matrix into a
+// swizzled LDS tile, straight from global memory to LDS (no registers).
+// Each wave instruction fills one contiguous KiB: lane i writes bytes
+// [16 i, 16 i + 16), so lane i fetches the global chunk that belongs there.
+// Rows past N read row N - 1 (finite data the callers mask or ignore).
+// Completion: s_waitcnt vmcnt(0) then a workgroup barrier.
+template <int D, int ROWS, int NWAVES>
+__device__ __forceinline__ void tile_load_async(uint8_t* tile, const uint16_t* __restrict__ X, int r0, int N,
+                                                int wave, int lane) {
+  constexpr int RPK = 1024 / (2 * D);   // rows per KiB
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int NK = ROWS / RPK;        // KiB pieces per tile
+  static_assert(NK % NWAVES == 0, "tile pieces per wave");
+#pragma unroll
+  for (int i = 0; i < NK / NWAVES; ++i) {
+    const int ci = wave + i * NWAVES;
+    const int row = ci * RPK + lane / CPR;
+    const int c = (lane % CPR) ^ swz<D>(row);
+    int gr = r0 + row;
+    gr = gr < N ? gr : N - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(X + (size_t)gr * D + c * 8), (lds_void*)(tile + ci * 1024),
+                                     16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A operand taken along the rows of a swizzled tile: lane (r = l % 32,
+// h = l / 32) gets row row0 + r, elements [16 ks + 8 h, +8).
+template <int D>
+__device__ __forceinline__ u32x4 tile_row_frag(const uint8_t* tile, int row0, int r, int h, int ks) {
+  return *(const u32x4*)(tile + tile_off<D>(row0 + r, ks * 16 + h * 8));
+}
+
+// A operand taken down the columns of a swizzled tile (the tile transposed):
+// lane (m = l % 32, h = l / 32) gets column col0 + m at the 8 rows
+// row0 + {4h..4h+3, 8+4h..8+4h+3}, the contraction slots a B operand built
+// from an MFMA C layout occupies. Two transpose reads: within each 16-lane
+// group, lane i receives element i % 4 of the 8-byte chunks addressed by
+// lanes 4 j + i / 4 (j = 0..3), so lane s of group g addresses row
+// row0 + 8 sel + 4 (g / 2) + (s % 16) / 4, columns col0 + 16 (g % 2) + 4 (s % 4).
+template <int D>
+__device__ __forceinline__ u32x4 tile_col_frag(const uint8_t* tile, int row0, int col0, int lane) {
+  const int g = lane >> 4, jj = (lane >> 2) & 3, q = lane & 3;
+  const int rl = 4 * (g >> 1) + jj;
+  const int cl = col0 + 16 * (g & 1) + 4 * q;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off<D>(row0 + rl, cl)));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off<D>(row0 + 8 + rl, cl)));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
 
 // Workgroup id -> logical tile id so that consecutive logical tiles (the query
 // tiles of one head) run on the same XCD and share its L2. Hardware hands out

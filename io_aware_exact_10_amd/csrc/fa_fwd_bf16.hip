@@ -7,23 +7,26 @@
 // row log-sum-exp are written; the N x N scores stay in registers.
 //
 // Work decomposition: one 256-thread workgroup per (query tile of 128 rows,
-// batch, head); each of the 4 waves owns 32 query rows, and the query tile
-// is parallel over the sequence ("Core ideas": parallelism over the sequence
+// batch, head); each of the 4 waves owns 32 query rows, and query tiles run
+// in parallel over the sequence ("Core ideas": parallelism over the sequence
 // dimension). The workgroup streams 64-key tiles of K and V through LDS,
-// double-buffered: global loads of tile t+1 are issued into registers before
-// tile t is computed and stored to the other LDS buffer afterwards.
+// double-buffered: tile t+1 is copied global -> LDS asynchronously (no
+// registers) while tile t is computed.
 //
 // Per wave and key tile (two 32-key sub-blocks):
 //   S^T = K Q^T     A = K rows from LDS, B = Q fragment held in registers.
 //                   The C layout puts one query per lane (n = lane % 32) and
 //                   16 keys per lane, so the row max and row sum are
 //                   lane-local plus one exchange with lane ^ 32.
-//   online softmax  m' = max(m, c * rowmax), alpha = 2^(m - m'),
-//                   p = 2^(c*s - m'), l = alpha*l + rowsum p, acc *= alpha,
-//                   with c = |scale| * log2(e) folded into one FMA.
+//   online softmax  p = 2^(c*s - m) with c = |scale| * log2(e) folded into
+//                   one FMA. The reference max m is raised only when some row
+//                   of the wave exceeds it by more than 8 (in log2 units);
+//                   then acc and l are multiplied by 2^(m_old - m_new). Any
+//                   reference max gives the same O = acc / l; this one keeps
+//                   p <= 2^8 and skips almost every rescale.
 //   O^T += V^T P^T  B = P^T straight from the S^T registers (rounded to
-//                   bf16), A = V^T read from a transposed LDS copy whose key
-//                   order matches the contraction slots P^T occupies.
+//                   bf16), A = V^T read from the row-major V tile with LDS
+//                   transpose reads, in the key order P^T occupies.
 // Epilogue: O = acc / l, LSE = ln 2 * (m + log2 l).
 #include "fa_common.h"
 #include "fa_kernels.h"
@@ -37,31 +40,17 @@ constexpr int kMaskBlock = 128;  // block-sparse mask granularity
 
 template <int D>
 struct alignas(16) FwdSmem {
-  static constexpr int KS = D + 8;        // K row stride in bf16 (pad: conflict-free b128 reads)
-  static constexpr int VS = kFwdBC + 8;   // V^T row stride in bf16
-  uint16_t k[2][kFwdBC * KS];
-  uint16_t vt[2][D * VS];
+  uint8_t k[2][kFwdBC * D * 2];   // swizzled row-major K tiles
+  uint8_t v[2][kFwdBC * D * 2];   // swizzled row-major V tiles
 };
 
-// Key position inside the transposed V tile. Within each group of 16 keys the
-// second and third quads swap, so the 8 keys that lane half h holds in its
-// P^T registers (keys 4h..4h+3 and 8+4h..8+4h+3) are contiguous at 8h.
-__device__ __forceinline__ int vt_quad_pos(int kq) {
-  const int q4 = kq & 3;
-  return (kq & ~3) + (q4 == 1 ? 2 : (q4 == 2 ? 1 : q4));
-}
+constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 template <int D, int MASK>
-__global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
+__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   __shared__ FwdSmem<D> sm;
-  constexpr int KS = FwdSmem<D>::KS;
-  constexpr int VS = FwdSmem<D>::VS;
-  constexpr int DC = D / 8;                                // 16-byte chunks per row
-  constexpr int KCH = kFwdBC * DC / kFwdThreads;           // K chunks per thread
-  constexpr int VUNITS = (kFwdBC / 4) * DC;                // 4-key x 8-column transpose units
   constexpr int TPB = kMaskBlock / kFwdBC;                 // key tiles per mask block
   constexpr int NDT = D / 32;                              // 32-row blocks of O^T
-  static_assert(KCH >= 1 && VUNITS <= kFwdThreads, "tile shape");
 
   const int N = p.N;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -79,15 +68,6 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(AttnParams p, uin
   const int qw0 = q0 + w * 32;
   const int qi = qw0 + r;
 
-  // Q fragment: B operand of S^T = K Q^T (lane: query qi, 8 consecutive d).
-  u32x4 qf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < N) x = *(const u32x4*)(Qh + (size_t)qi * D + ks * 16 + h * 8);
-    qf[ks] = x ^ p.qflip;
-  }
-
   const int nkt = (N + kFwdBC - 1) / kFwdBC;
   int kend = nkt;
   if (MASK == 1) kend = min(nkt, (q0 + kFwdBR + kFwdBC - 1) / kFwdBC);
@@ -101,56 +81,27 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(AttnParams p, uin
     const int t = nb == blk ? kt : nb * TPB;
     return t < kend ? t : kend;
   };
+  auto issue = [&](int kt, int buf) {
+    tile_load_async<D, kFwdBC, 4>(sm.k[buf], Kh, kt * kFwdBC, N, w, lane);
+    tile_load_async<D, kFwdBC, 4>(sm.v[buf], Vh, kt * kFwdBC, N, w, lane);
+  };
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[4];
-  auto gload = [&](int kt) {
-    const int k0 = kt * kFwdBC;
+  int kt = next_tile(0);
+  if (kt < kend) issue(kt, 0);
+
+  // Q fragment: B operand of S^T = K Q^T (lane: query qi, 8 consecutive d).
+  u32x4 qf[D / 16];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * kFwdThreads;
-      const int row = c / DC, col = c % DC;
-      const int key = k0 + row;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < N) x = *(const u32x4*)(Kh + (size_t)key * D + col * 8);
-      kreg[i] = x;
-    }
-    if (tid < VUNITS) {
-      const int dc = tid % DC, kq = tid / DC;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + kq * 4 + j;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < N) x = *(const u32x4*)(Vh + (size_t)key * D + dc * 8);
-        vreg[j] = x;
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * kFwdThreads;
-      const int row = c / DC, col = c % DC;
-      *(u32x4*)&sm.k[buf][row * KS + col * 8] = kreg[i];
-    }
-    if (tid < VUNITS) {
-      const int dc = tid % DC, kq = tid / DC;
-      const int pos = vt_quad_pos(kq) * 4;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t a0 = vreg[0][jj], a1 = vreg[1][jj], a2 = vreg[2][jj], a3 = vreg[3][jj];
-        u32x2 lo = {lo_halves(a0, a1), lo_halves(a2, a3)};
-        u32x2 hi = {hi_halves(a0, a1), hi_halves(a2, a3)};
-        *(u32x2*)&sm.vt[buf][(dc * 8 + 2 * jj) * VS + pos] = lo;
-        *(u32x2*)&sm.vt[buf][(dc * 8 + 2 * jj + 1) * VS + pos] = hi;
-      }
-    }
-  };
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (qi < N) x = *(const u32x4*)(Qh + (size_t)qi * D + ks * 16 + h * 8);
+    qf[ks] = x ^ p.qflip;
+  }
 
   f32x16 acc[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) acc[i] = zero16();
-  float m_run = -INFINITY;   // running max of c*s (exp2 domain), per query
+  float m_run = -INFINITY;   // reference max of c*s (exp2 domain), per query
   float l_run = 0.f;         // this lane's partial running sum (its 16-key half)
   const float c = p.c;
 
@@ -168,30 +119,22 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(AttnParams p, uin
       s[kb] = zero16();
       if (live[kb]) {
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const u32x4 a = *(const u32x4*)&sm.k[buf][(kb * 32 + r) * KS + ks * 16 + h * 8];
-          s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
-        }
+        for (int ks = 0; ks < D / 16; ++ks)
+          s[kb] = mfma_32x32x16(tile_row_frag<D>(sm.k[buf], kb * 32, r, h, ks), qf[ks], s[kb]);
       }
     }
 
-    float m_new, m_use;
-    float pv[2][16];
+    // Scores to the exp2 domain (masked entries -inf) and the tile row max.
+    float mx;
     if (!need_mask) {
-      float mx = -INFINITY;
+      mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      m_new = fmaxf(m_run, mx * c);
-      m_use = m_new == -INFINITY ? 0.f : m_new;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pv[kb][i] = fast_exp2(__builtin_fmaf(s[kb][i], c, -m_use));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
     } else {
-      float mx = -INFINITY;
+      mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -199,39 +142,42 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(AttnParams p, uin
           const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
           const bool vis = live[kb] && key < N && (MASK != 1 || key <= qi);
           const float t = vis ? s[kb][i] * c : -INFINITY;
-          pv[kb][i] = t;
+          s[kb][i] = t;
           mx = fmaxf(mx, t);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      m_new = fmaxf(m_run, mx);
-      m_use = m_new == -INFINITY ? 0.f : m_new;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pv[kb][i] = fast_exp2(pv[kb][i] - m_use);
     }
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float rs = 0.f;
+    // Raise the reference max only when some row of the wave outgrows it.
+    if (__ballot(mx > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);   // 0 on the first update
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) rs += pv[kb][i];
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
-    // P^T as the B operand: registers 8s..8s+7 of sub-block kb form k-step s.
+    // P^T as the B operand: registers 8st..8st+7 of sub-block kb form k-step st.
     u32x4 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const float* x = &pv[kb][8 * st];
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sv = s[kb][8 * st + e];
+          x[e] = need_mask ? fast_exp2(sv - m_use) : fast_exp2(__builtin_fmaf(sv, c, -m_use));
+        }
         pb[kb][st] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                            pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+        // fp32 row sum of the unrounded p: the log-sum-exp must not carry the
+        // bf16 rounding of P.
+#pragma unroll
+        for (int e = 0; e < 8; ++e) l_run += x[e];
       }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -239,26 +185,20 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(AttnParams p, uin
       for (int kb = 0; kb < 2; ++kb) {
         if (!live[kb]) continue;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 a = *(const u32x4*)&sm.vt[buf][(dt * 32 + r) * VS + kb * 32 + st * 16 + h * 8];
-          acc[dt] = mfma_32x32x16(a, pb[kb][st], acc[dt]);
-        }
+        for (int st = 0; st < 2; ++st)
+          acc[dt] = mfma_32x32x16(tile_col_frag<D>(sm.v[buf], kb * 32 + st * 16, dt * 32, lane), pb[kb][st],
+                                  acc[dt]);
       }
   };
 
-  int kt = next_tile(0);
-  if (kt < kend) {
-    gload(kt);
-    sstore(0);
-  }
+  wait_vmem();
   __syncthreads();
   int buf = 0;
   while (kt < kend) {
     const int ktn = next_tile(kt + 1);
-    const bool more = ktn < kend;
-    if (more) gload(ktn);
+    if (ktn < kend) issue(ktn, buf ^ 1);
     compute(buf, kt);
-    if (more) sstore(buf ^ 1);
+    wait_vmem();
     __syncthreads();
     buf ^= 1;
     kt = ktn;
