@@ -14,18 +14,24 @@
 //   bwd_rowterm   D_i = sum_k dO_ik O_ik (a streaming pass over O and dO).
 //   bwd_dkdv      one workgroup per 128-key tile (32 keys per wave), looping
 //                 over the visible 64-query tiles: K and V stay in registers
-//                 as MFMA B operands, Q and dO tiles stream through LDS in
-//                 row-major and transposed copies; dK^T and dV^T accumulate
-//                 in registers and are written once.
+//                 as MFMA B operands; each Q and dO tile is copied once,
+//                 global -> LDS, into a swizzled row-major tile that serves
+//                 both as a row operand (S = Q K^T, dP = dO V^T) and, through
+//                 LDS transpose reads, as a column operand (dV^T = dO^T P,
+//                 dK^T = Q^T dS); dK^T and dV^T accumulate in registers and
+//                 are written once.
 //   bwd_dq        one workgroup per 128-query tile (32 queries per wave),
 //                 looping over the visible 64-key tiles: Q and dO stay in
-//                 registers, K (row-major and transposed) and V stream
-//                 through LDS; dQ^T accumulates in registers and is written
-//                 once. dQ is thus accumulated separately from dK/dV and
-//                 without atomics, so results are deterministic.
+//                 registers; K and V tiles stream through LDS the same way
+//                 (K read along rows for S^T and down columns for
+//                 dQ^T = K^T dS^T); dQ^T accumulates in registers and is
+//                 written once. dQ is thus accumulated separately from dK/dV
+//                 and without atomics, so results are deterministic.
 // In both loop kernels the scores are formed so that the C layout puts the
 // index of the *accumulated* output (a key for dK/dV, a query for dQ) on the
 // lane, which lets P and dS feed the next product as B operands directly.
+// Both loop kernels double-buffer their LDS tiles: tile t+1 is copied while
+// tile t is computed.
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -33,27 +39,6 @@ namespace fa {
 
 constexpr int kThreads = 256;
 constexpr int kMaskBlk = 128;
-
-// Same key/query position swap as the forward's V^T tile: within each group
-// of 16, quads 1 and 2 trade places so the 8 contraction slots of lane half h
-// are contiguous at offset 8h.
-__device__ __forceinline__ int quad_pos(int kq) {
-  const int q4 = kq & 3;
-  return (kq & ~3) + (q4 == 1 ? 2 : (q4 == 2 ? 1 : q4));
-}
-
-// Stores a 4-row x 8-column bf16 block (x[j] = row j, 8 columns) transposed:
-// column c of the block goes to t[(col0 + c) * ts + pos .. + 3].
-__device__ __forceinline__ void store_quad_transposed(uint16_t* t, int ts, int col0, int pos, const u32x4 x[4]) {
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const uint32_t a0 = x[0][jj], a1 = x[1][jj], a2 = x[2][jj], a3 = x[3][jj];
-    u32x2 lo = {lo_halves(a0, a1), lo_halves(a2, a3)};
-    u32x2 hi = {hi_halves(a0, a1), hi_halves(a2, a3)};
-    *(u32x2*)&t[(col0 + 2 * jj) * ts + pos] = lo;
-    *(u32x2*)&t[(col0 + 2 * jj + 1) * ts + pos] = hi;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // row term D = rowsum(dO * O), fp32 accumulation
@@ -87,27 +72,20 @@ constexpr int kDkvBQ = 64;    // queries per LDS tile
 
 template <int D>
 struct alignas(16) DkvSmem {
-  static constexpr int RS = D + 8;
-  static constexpr int TS = kDkvBQ + 8;
-  uint16_t q[2][kDkvBQ * RS];
-  uint16_t dO[2][kDkvBQ * RS];
-  uint16_t qt[2][D * TS];
-  uint16_t dOt[2][D * TS];
-  float lse2[2][kDkvBQ];
+  uint8_t q[2][kDkvBQ * D * 2];    // swizzled row-major Q tiles (sign-adjusted on read)
+  uint8_t dO[2][kDkvBQ * D * 2];   // swizzled row-major dO tiles
+  float lse[2][kDkvBQ];
   float dterm[2][kDkvBQ];
 };
 
+// d = 128 keeps K, V fragments and the dK^T, dV^T accumulators (192 VGPRs)
+// resident, so it runs one wave per SIMD; d = 64 fits two.
 template <int D, int MASK>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2)))
+void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   __shared__ DkvSmem<D> sm;
-  constexpr int RS = DkvSmem<D>::RS;
-  constexpr int TS = DkvSmem<D>::TS;
-  constexpr int DC = D / 8;
-  constexpr int UNITS = (kDkvBQ / 4) * DC;             // 4-row x 8-col units per tensor
-  constexpr int UPT = (2 * UNITS) / kThreads;          // units per thread (Q and dO together)
   constexpr int NDT = D / 32;
   constexpr int QPB = kMaskBlk / kDkvBQ;               // query tiles per mask block
-  static_assert(UPT >= 1 && (2 * UNITS) % kThreads == 0, "tile shape");
 
   const int N = p.N;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -126,18 +104,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(AttnParams p, u
   const float* __restrict__ lseh = p.lse + (size_t)bh * N;
   const float* __restrict__ dth = p.dterm + (size_t)bh * N;
 
-  u32x4 kf[D / 16], vf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (kj < N) {
-      a = *(const u32x4*)(Kh + (size_t)kj * D + ks * 16 + h * 8);
-      b = *(const u32x4*)(Vh + (size_t)kj * D + ks * 16 + h * 8);
-    }
-    kf[ks] = a;
-    vf[ks] = b;
-  }
-
   const int nqt = (N + kDkvBQ - 1) / kDkvBQ;
   const int qbeg = MASK == 1 ? k0 / kDkvBQ : 0;
   MaskScan ms;
@@ -150,57 +116,32 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(AttnParams p, u
     const int t = nb == blk ? it : nb * QPB;
     return t < nqt ? t : nqt;
   };
-
-  u32x4 reg[UPT][4];
-  float lreg = 0.f, dreg = 0.f;
-  auto gload = [&](int it) {
+  auto issue = [&](int it, int buf) {
     const int q0 = it * kDkvBQ;
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * kThreads;
-      const int which = unit / UNITS, uu = unit % UNITS;
-      const int dc = uu % DC, kq = uu / DC;
-      const uint16_t* src = which == 0 ? Qh : dOh;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int q = q0 + kq * 4 + j;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (q < N) x = *(const u32x4*)(src + (size_t)q * D + dc * 8);
-        reg[u][j] = x;
-      }
-    }
-    if (tid < kDkvBQ) {
-      const int q = q0 + tid;
-      float l2 = INFINITY, dv = 0.f;   // rows past N: P = 2^-inf = 0
-      if (q < N) {
-        const float l = lseh[q];
-        l2 = l == -INFINITY ? INFINITY : l * kLog2e;
-        dv = dth[q];
-      }
-      lreg = l2;
-      dreg = dv;
+    tile_load_async<D, kDkvBQ, 4>(sm.q[buf], Qh, q0, N, w, lane);
+    tile_load_async<D, kDkvBQ, 4>(sm.dO[buf], dOh, q0, N, w, lane);
+    if (w < 2) {   // one dword per lane: 64 row statistics per tile
+      const int q = min(q0 + lane, N - 1);
+      const float* src = w == 0 ? lseh + q : dth + q;
+      float* dst = w == 0 ? sm.lse[buf] : sm.dterm[buf];
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 4, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
+
+  int it = next_tile(qbeg);
+  if (it < nqt) issue(it, 0);
+
+  u32x4 kf[D / 16], vf[D / 16];
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * kThreads;
-      const int which = unit / UNITS, uu = unit % UNITS;
-      const int dc = uu % DC, kq = uu / DC;
-      u32x4 x[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = which == 0 ? (reg[u][j] ^ p.qflip) : reg[u][j];
-      uint16_t* rm = which == 0 ? sm.q[buf] : sm.dO[buf];
-      uint16_t* tr = which == 0 ? sm.qt[buf] : sm.dOt[buf];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *(u32x4*)&rm[(kq * 4 + j) * RS + dc * 8] = x[j];
-      store_quad_transposed(tr, TS, dc * 8, quad_pos(kq) * 4, x);
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (kj < N) {
+      a = *(const u32x4*)(Kh + (size_t)kj * D + ks * 16 + h * 8);
+      b = *(const u32x4*)(Vh + (size_t)kj * D + ks * 16 + h * 8);
     }
-    if (tid < kDkvBQ) {
-      sm.lse2[buf][tid] = lreg;
-      sm.dterm[buf][tid] = dreg;
-    }
-  };
+    kf[ks] = a ^ p.qflip;   // S = |scale| Q (sign(scale) K)^T: the sign of scale rides on K here
+    vf[ks] = b;
+  }
 
   f32x16 dkT[NDT], dvT[NDT];
 #pragma unroll
@@ -212,98 +153,72 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(AttnParams p, u
 
   auto compute = [&](int buf, int it) {
     const int q0 = it * kDkvBQ;
-    bool live[2], needm[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int qb0 = q0 + 32 * mb;
-      live[mb] = !(MASK == 1 && qb0 + 31 < kw0);
-      needm[mb] = MASK == 1 && qb0 < kw0 + 31;
-    }
-    if (!live[0] && !live[1]) return;
-    f32x16 s[2], dp[2];
+      if (MASK == 1 && qb0 + 31 < kw0) continue;           // every query before this wave's keys
+      const bool needm = (MASK == 1 && qb0 < kw0 + 31) || qb0 + 32 > N;
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = zero16();
-      dp[mb] = zero16();
-      if (!live[mb]) continue;
+      for (int ks = 0; ks < D / 16; ++ks)
+        s = mfma_32x32x16(tile_row_frag<D>(sm.q[buf], mb * 32, r, h, ks), kf[ks], s);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 aq = *(const u32x4*)&sm.q[buf][(mb * 32 + r) * RS + ks * 16 + h * 8];
-        s[mb] = mfma_32x32x16(aq, kf[ks], s[mb]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 ao = *(const u32x4*)&sm.dO[buf][(mb * 32 + r) * RS + ks * 16 + h * 8];
-        dp[mb] = mfma_32x32x16(ao, vf[ks], dp[mb]);
-      }
-    }
-    u32x4 pb[2][2], db[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      float pv[16], dv[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = mb * 32 + 8 * g + 4 * h;
-        const float4 l4 = *(const float4*)&sm.lse2[buf][ql];
-        const float4 d4 = *(const float4*)&sm.dterm[buf][ql];
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          float pp = fast_exp2(__builtin_fmaf(s[mb][i], c, -lv[e]));
-          if (needm[mb] && kj > q0 + ql + e) pp = 0.f;
-          if (!live[mb]) pp = 0.f;
-          pv[i] = pp;
-          dv[i] = pp * (dp[mb][i] - dd[e]);
-        }
-      }
+      for (int ks = 0; ks < D / 16; ++ks)
+        dp = mfma_32x32x16(tile_row_frag<D>(sm.dO[buf], mb * 32, r, h, ks), vf[ks], dp);
+      u32x4 pb[2], db[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const float* x = &pv[8 * st];
-        const float* y = &dv[8 * st];
-        pb[mb][st] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                           pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
-        db[mb][st] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                           pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+        float pv[8], dv[8];
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g = 2 * st + g2;
+          const int ql = mb * 32 + 8 * g + 4 * h;
+          const float4 l4 = *(const float4*)&sm.lse[buf][ql];
+          const float4 d4 = *(const float4*)&sm.dterm[buf][ql];
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g + e;
+            float pp = fast_exp2(__builtin_fmaf(s[i], c, -lv[e] * kLog2e));
+            if (needm) {
+              const int q = q0 + ql + e;
+              if (q >= N || (MASK == 1 && kj > q)) pp = 0.f;
+            }
+            pv[4 * g2 + e] = pp;
+            dv[4 * g2 + e] = pp * (dp[i] - dd[e]);
+          }
+        }
+        pb[st] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                       pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+        db[st] = u32x4{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]),
+                       pack_bf16x2(dv[4], dv[5]), pack_bf16x2(dv[6], dv[7])};
       }
-    }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        if (!live[mb]) continue;
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const int off = (dt * 32 + r) * TS + mb * 32 + st * 16 + h * 8;
-          const u32x4 ao = *(const u32x4*)&sm.dOt[buf][off];
-          dvT[dt] = mfma_32x32x16(ao, pb[mb][st], dvT[dt]);
-          const u32x4 aq = *(const u32x4*)&sm.qt[buf][off];
-          dkT[dt] = mfma_32x32x16(aq, db[mb][st], dkT[dt]);
+          dvT[dt] = mfma_32x32x16(tile_col_frag<D>(sm.dO[buf], mb * 32 + st * 16, dt * 32, lane), pb[st], dvT[dt]);
+          dkT[dt] = mfma_32x32x16(tile_col_frag<D>(sm.q[buf], mb * 32 + st * 16, dt * 32, lane), db[st], dkT[dt]);
         }
-      }
+    }
   };
 
-  int it = next_tile(qbeg);
-  if (it < nqt) {
-    gload(it);
-    sstore(0);
-  }
+  wait_vmem();
   __syncthreads();
   int buf = 0;
   while (it < nqt) {
     const int itn = next_tile(it + 1);
-    const bool more = itn < nqt;
-    if (more) gload(itn);
+    if (itn < nqt) issue(itn, buf ^ 1);
     compute(buf, it);
-    if (more) sstore(buf ^ 1);
+    wait_vmem();
     __syncthreads();
     buf ^= 1;
     it = itn;
   }
 
   if (kj < N) {
-    const float ks = fabsf(p.scale);
+    const float sk = p.scale;   // dK = scale dS^T Q (Q unmodified; the sign of scale only entered S via kf)
     uint16_t* __restrict__ dKrow = (uint16_t*)p.dk + hoff + (size_t)kj * D;
     uint16_t* __restrict__ dVrow = (uint16_t*)p.dv + hoff + (size_t)kj * D;
 #pragma unroll
@@ -311,8 +226,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(AttnParams p, u
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int dd = dt * 32 + 8 * g + 4 * h;
-        u32x2 a = {pack_bf16x2(dkT[dt][4 * g] * ks, dkT[dt][4 * g + 1] * ks),
-                   pack_bf16x2(dkT[dt][4 * g + 2] * ks, dkT[dt][4 * g + 3] * ks)};
+        u32x2 a = {pack_bf16x2(dkT[dt][4 * g] * sk, dkT[dt][4 * g + 1] * sk),
+                   pack_bf16x2(dkT[dt][4 * g + 2] * sk, dkT[dt][4 * g + 3] * sk)};
         u32x2 b = {pack_bf16x2(dvT[dt][4 * g], dvT[dt][4 * g + 1]),
                    pack_bf16x2(dvT[dt][4 * g + 2], dvT[dt][4 * g + 3])};
         *(u32x2*)(dKrow + dd) = a;
@@ -329,24 +244,16 @@ constexpr int kDqBK = 64;    // keys per LDS tile
 
 template <int D>
 struct alignas(16) DqSmem {
-  static constexpr int RS = D + 8;
-  static constexpr int TS = kDqBK + 8;
-  uint16_t k[2][kDqBK * RS];
-  uint16_t v[2][kDqBK * RS];
-  uint16_t kt[2][D * TS];
+  uint8_t k[2][kDqBK * D * 2];   // swizzled row-major K tiles
+  uint8_t v[2][kDqBK * D * 2];   // swizzled row-major V tiles
 };
 
 template <int D, int MASK>
-__global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   __shared__ DqSmem<D> sm;
-  constexpr int RS = DqSmem<D>::RS;
-  constexpr int TS = DqSmem<D>::TS;
-  constexpr int DC = D / 8;
-  constexpr int KUNITS = (kDqBK / 4) * DC;             // 4-key x 8-col units of K
-  constexpr int VCH = kDqBK * DC / kThreads;           // 16-byte V chunks per thread
   constexpr int NDT = D / 32;
   constexpr int TPB = kMaskBlk / kDqBK;
-  static_assert(KUNITS <= kThreads && VCH >= 1, "tile shape");
 
   const int N = p.N;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -363,6 +270,27 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(AttnParams p, uin
   const uint16_t* __restrict__ Kh = (const uint16_t*)p.k + hoff;
   const uint16_t* __restrict__ Vh = (const uint16_t*)p.v + hoff;
   const uint16_t* __restrict__ dOh = (const uint16_t*)p.dO + hoff;
+
+  const int nkt = (N + kDqBK - 1) / kDqBK;
+  int kend = nkt;
+  if (MASK == 1) kend = min(nkt, (q0 + kDqBQ + kDqBK - 1) / kDqBK);
+  MaskScan ms;
+  if (MASK == 2) ms.init(p.block_mask + (size_t)qt * p.nblk, 1, p.nblk);
+  auto next_tile = [&](int kt) -> int {
+    if (MASK != 2 || kt >= kend) return kt < kend ? kt : kend;
+    const int blk = kt / TPB;
+    const int nb = ms.next(blk);
+    if (nb >= p.nblk) return kend;
+    const int t = nb == blk ? kt : nb * TPB;
+    return t < kend ? t : kend;
+  };
+  auto issue = [&](int kt, int buf) {
+    tile_load_async<D, kDqBK, 4>(sm.k[buf], Kh, kt * kDqBK, N, w, lane);
+    tile_load_async<D, kDqBK, 4>(sm.v[buf], Vh, kt * kDqBK, N, w, lane);
+  };
+
+  int kt = next_tile(0);
+  if (kt < kend) issue(kt, 0);
 
   u32x4 qf[D / 16], of[D / 16];
 #pragma unroll
@@ -382,58 +310,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(AttnParams p, uin
     dti = p.dterm[(size_t)bh * N + qi];
   }
 
-  const int nkt = (N + kDqBK - 1) / kDqBK;
-  int kend = nkt;
-  if (MASK == 1) kend = min(nkt, (q0 + kDqBQ + kDqBK - 1) / kDqBK);
-  MaskScan ms;
-  if (MASK == 2) ms.init(p.block_mask + (size_t)qt * p.nblk, 1, p.nblk);
-  auto next_tile = [&](int kt) -> int {
-    if (MASK != 2 || kt >= kend) return kt < kend ? kt : kend;
-    const int blk = kt / TPB;
-    const int nb = ms.next(blk);
-    if (nb >= p.nblk) return kend;
-    const int t = nb == blk ? kt : nb * TPB;
-    return t < kend ? t : kend;
-  };
-
-  u32x4 kreg[4], vreg[VCH];
-  auto gload = [&](int kt) {
-    const int k0 = kt * kDqBK;
-    if (tid < KUNITS) {
-      const int dc = tid % DC, kq = tid / DC;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + kq * 4 + j;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < N) x = *(const u32x4*)(Kh + (size_t)key * D + dc * 8);
-        kreg[j] = x;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx / DC, col = cidx % DC;
-      const int key = k0 + row;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < N) x = *(const u32x4*)(Vh + (size_t)key * D + col * 8);
-      vreg[i] = x;
-    }
-  };
-  auto sstore = [&](int buf) {
-    if (tid < KUNITS) {
-      const int dc = tid % DC, kq = tid / DC;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *(u32x4*)&sm.k[buf][(kq * 4 + j) * RS + dc * 8] = kreg[j];
-      store_quad_transposed(sm.kt[buf], TS, dc * 8, quad_pos(kq) * 4, kreg);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx / DC, col = cidx % DC;
-      *(u32x4*)&sm.v[buf][row * RS + col * 8] = vreg[i];
-    }
-  };
-
   f32x16 dqT[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) dqT[i] = zero16();
@@ -443,79 +319,56 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(AttnParams p, uin
     const int k0 = kt * kDqBK;
     if (MASK == 1 && k0 > qw0 + 31) return;
     const bool need_mask = (k0 + kDqBK > N) || (MASK == 1 && k0 + kDqBK - 1 > qw0);
-    bool live[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) live[kb] = !(MASK == 1 && k0 + kb * 32 > qw0 + 31);
-    f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
-      dp[kb] = zero16();
-      if (!live[kb]) continue;
+      if (MASK == 1 && k0 + kb * 32 > qw0 + 31) continue;
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 a = *(const u32x4*)&sm.k[buf][(kb * 32 + r) * RS + ks * 16 + h * 8];
-        s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
-      }
+      for (int ks = 0; ks < D / 16; ++ks)
+        s = mfma_32x32x16(tile_row_frag<D>(sm.k[buf], kb * 32, r, h, ks), qf[ks], s);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 a = *(const u32x4*)&sm.v[buf][(kb * 32 + r) * RS + ks * 16 + h * 8];
-        dp[kb] = mfma_32x32x16(a, of[ks], dp[kb]);
-      }
-    }
-    u32x4 db[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float dv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pp = fast_exp2(__builtin_fmaf(s[kb][i], c, -lse2));
-        if (need_mask) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (!live[kb] || key >= N || (MASK == 1 && key > qi)) pp = 0.f;
-        }
-        dv[i] = pp * (dp[kb][i] - dti);
-      }
+      for (int ks = 0; ks < D / 16; ++ks)
+        dp = mfma_32x32x16(tile_row_frag<D>(sm.v[buf], kb * 32, r, h, ks), of[ks], dp);
+      u32x4 db[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const float* y = &dv[8 * st];
-        db[kb][st] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                           pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
-      }
-    }
+        float y[8];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (!live[kb]) continue;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 a = *(const u32x4*)&sm.kt[buf][(dt * 32 + r) * TS + kb * 32 + st * 16 + h * 8];
-          dqT[dt] = mfma_32x32x16(a, db[kb][st], dqT[dt]);
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * st + e;
+          float pp = fast_exp2(__builtin_fmaf(s[i], c, -lse2));
+          if (need_mask) {
+            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (key >= N || (MASK == 1 && key > qi)) pp = 0.f;
+          }
+          y[e] = pp * (dp[i] - dti);
         }
+        db[st] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                       pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
       }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          dqT[dt] = mfma_32x32x16(tile_col_frag<D>(sm.k[buf], kb * 32 + st * 16, dt * 32, lane), db[st], dqT[dt]);
+    }
   };
 
-  int kt = next_tile(0);
-  if (kt < kend) {
-    gload(kt);
-    sstore(0);
-  }
+  wait_vmem();
   __syncthreads();
   int buf = 0;
   while (kt < kend) {
     const int ktn = next_tile(kt + 1);
-    const bool more = ktn < kend;
-    if (more) gload(ktn);
+    if (ktn < kend) issue(ktn, buf ^ 1);
     compute(buf, kt);
-    if (more) sstore(buf ^ 1);
+    wait_vmem();
     __syncthreads();
     buf ^= 1;
     kt = ktn;
   }
 
   if (qi < N) {
-    const float sc = p.scale;
+    const float sc = p.scale;   // dQ = scale dS K (K unmodified; the sign of scale only entered S via qf)
     uint16_t* __restrict__ dQrow = (uint16_t*)p.dq + hoff + (size_t)qi * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
