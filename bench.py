@@ -10,9 +10,16 @@ timed region starts.
 Prints ONE JSON line (rank 0) with the metric in TFLOP/s under the FLOP
 convention fwd = 4*d*vis, bwd = 10*d*vis per head (vis = visible
 query/key pairs), plus:
-  roofline      the forward kernel's achieved TFLOP/s (algorithmic FLOPs per
-                launch / its mean duration from HIP events on the launch
-                stream) against the MI355X dense bf16 MFMA peak;
+  kernels       each kernel's mean duration per step from HIP events on the
+                launch stream (the backward is enqueued as its three steps,
+                fa_bwd_rowterm, fa_bwd_dkdv and fa_bwd_dq, the exact work
+                fa_bwd does) and its algorithmic FLOPs per launch: fwd
+                4*d*vis, dK/dV 8*d*vis (S, dP, dV, dK), dQ 2*d*vis (its S
+                and dP are recomputation and not counted);
+  roofline      the dominant (longest) kernel's achieved TFLOP/s against the
+                MI355X dense bf16 MFMA peak, with its HBM traffic per launch
+                from rocprofv3 FETCH_SIZE + WRITE_SIZE (profiles/traffic.json)
+                when those counters were taken on the current source;
   cpu_baseline  the float64 CPU oracle timed on a bounded sample of the same
                 workload on this host's cores;
   naive         the materialise-S torch composition (matmul, mask, softmax,
@@ -39,6 +46,13 @@ PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 2516.6: 256 CUs x 2.4 GHz x 4
 PEAK_F32_VALU_TFLOPS = 157.3
 A100_FIG2_MS = 7.3                                # the pages' GPT-2-medium attention runtime (context)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "rowterm": "bwd_rowterm_bf16_kernel",
+                "dkdv": "bwd_dkdv_bf16_kernel", "dq": "bwd_dq_bf16_kernel"}
+_CSRC = "io_aware_exact_10_amd/csrc/"
+KERNEL_SOURCES = {"fwd": (_CSRC + "fa_fwd_bf16.hip", _CSRC + "fa_common.h"),
+                  "rowterm": (_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_common.h"),
+                  "dkdv": (_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_common.h"),
+                  "dq": (_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_common.h")}
 
 
 def visible_pairs(w: synth.Workload, mask: np.ndarray | None) -> int:
@@ -110,6 +124,69 @@ def naive_step(q, k, v, do, scale, mask_kind, bool_mask, backward):
     return o
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (text for profiles/), read from the SQLite output
+# ---------------------------------------------------------------------------
+KEYS_BY_SUBSTR = (("fwd_bf16_kernel", "fwd"), ("bwd_rowterm_bf16_kernel", "rowterm"),
+                  ("bwd_dkdv_bf16_kernel", "dkdv"), ("bwd_dq_bf16_kernel", "dq"))
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def summarize_trace(db_path: str) -> str:
+    import sqlite3
+    cur = sqlite3.connect(db_path).cursor()
+    rows = cur.execute("select name, total_calls, average, percentage from top_kernels").fetchall()
+    out = ["| kernel | calls | mean duration (us) | share of GPU time (%) |", "|---|---|---|---|"]
+    for name, calls, avg, pct in rows:
+        out.append(f"| `{name}` | {calls} | {avg:.2f} | {pct:.1f} |")
+    return "\n".join(out)
+
+
+def _pmc_means(db_path: str, counter: str) -> dict:
+    import collections
+    import sqlite3
+    cur = sqlite3.connect(db_path).cursor()
+    acc = collections.defaultdict(float)
+    disp = collections.defaultdict(set)
+    for name, did, val in cur.execute(
+            "select kernel_name, dispatch_id, value from counters_collection where counter_name = ?", (counter,)):
+        acc[name] += val
+        disp[name].add(did)
+    return {n: acc[n] / len(disp[n]) for n in acc}
+
+
+def summarize_traffic(fetch_db: str, write_db: str, workload: str, copy_bytes: int, update: bool) -> str:
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for a copy of copy_bytes."""
+    fetch = _pmc_means(fetch_db, "FETCH_SIZE")
+    write = _pmc_means(write_db, "WRITE_SIZE")
+    cf = fetch.get(next((n for n in fetch if COPY_KERNEL in n), ""), None)
+    cw = write.get(next((n for n in write if COPY_KERNEL in n), ""), None)
+    if not cf or not cw:
+        raise SystemExit("copy calibration kernel not found in the counter databases")
+    f_scale = copy_bytes / (cf * 1024.0)      # true bytes per counted byte
+    w_scale = copy_bytes / (cw * 1024.0)
+    lines = [f"copy of {copy_bytes} B: FETCH_SIZE {cf:.0f} KiB (scale {f_scale:.4f}), "
+             f"WRITE_SIZE {cw:.0f} KiB (scale {w_scale:.4f})", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |", "|---|---|---|---|"]
+    rec = json.load(open(PROFILE_TRAFFIC)) if os.path.exists(PROFILE_TRAFFIC) else {}
+    entry = rec.setdefault(workload, {})
+    for sub, key in KEYS_BY_SUBSTR:
+        fn = next((n for n in fetch if sub in n), None)
+        wn = next((n for n in write if sub in n), None)
+        if fn is None or wn is None:
+            continue
+        b = fetch[fn] * 1024.0 * f_scale + write[wn] * 1024.0 * w_scale
+        lines.append(f"| `{fn}` | {fetch[fn]:.0f} | {write[wn]:.0f} | {b:.4g} |")
+        entry[key] = {"hbm_bytes_per_launch": round(b), "fetch_kib": round(fetch[fn]), "write_kib": round(write[wn]),
+                      "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+                      "source_digest": source_digest(*KERNEL_SOURCES[key])}
+    if update:
+        os.makedirs(os.path.dirname(PROFILE_TRAFFIC), exist_ok=True)
+        json.dump(rec, open(PROFILE_TRAFFIC, "w"), indent=1, sort_keys=True)
+    return "\n".join(lines)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,7 +196,21 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after the run, copy BYTES once more between two device buffers (counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DB", help="print a kernel table from a rocprofv3 trace database")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="HBM bytes per launch from FETCH_SIZE / WRITE_SIZE counter databases")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--update-traffic", action="store_true", help="write the result into profiles/traffic.json")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic, args.workload, args.copy_bytes, args.update_traffic))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -165,8 +256,11 @@ def main() -> int:
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
+    # The timed step enqueues fa_fwd and the three steps of fa_bwd one by one,
+    # with a HIP event between launches on the launch stream.
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    names = ["fwd"] + (["rowterm", "dkdv", "dq"] if backward else [])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -174,15 +268,18 @@ def main() -> int:
         fa.forward(q, k, v, w.scale, w.mask_kind, mask_t, out=o, lse=lse)
         ev[i][1].record(stream)
         if backward:
-            fa.backward(q, k, v, o, lse, do, w.scale, w.mask_kind, mask_t, workspace=ws, dq=dq, dk=dk, dv=dv)
-        ev[i][2].record(stream)
+            for j, st in enumerate(("rowterm", "dkdv", "dq")):
+                fa.backward(q, k, v, o, lse, do, w.scale, w.mask_kind, mask_t, workspace=ws, dq=dq, dk=dk, dv=dv,
+                            steps=st)
+                ev[i][2 + j].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])
-    bwd_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)])
+    per = {n: np.array([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]) for j, n in enumerate(names)}
+    fwd_ms = per["fwd"]
+    bwd_ms = sum(per[n] for n in names[1:]) if backward else np.zeros_like(fwd_ms)
     step_ms = fwd_ms + bwd_ms
-    print(f"# timed {args.steps} steps: {step_ms.mean():.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
-          file=sys.stderr, flush=True)
+    print(f"# timed {args.steps} steps: {step_ms.mean():.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}) "
+          + " ".join(f"{n} {per[n].mean():.3f}" for n in names), file=sys.stderr, flush=True)
 
     vis = visible_pairs(w, inp.mask)
     heads = w.B * w.H
@@ -194,17 +291,25 @@ def main() -> int:
     bwd_tflops = bwd_flop / (bwd_ms.mean() * 1e-3) / 1e12 if backward else None
 
     peak = PEAK_BF16_TFLOPS if w.dtype == synth.DTYPE_BF16 else PEAK_F32_VALU_TFLOPS
+    kflop = {"fwd": fwd_flop, "rowterm": 0.0, "dkdv": 8.0 * w.d * vis * heads, "dq": 2.0 * w.d * vis * heads}
+    kernels = {}
+    for n in names:
+        t = float(per[n].mean())
+        kernels[n] = {"kernel": KERNEL_NAMES[n], "mean_ms": round(t, 4), "algorithmic_gflop": round(kflop[n] / 1e9, 2),
+                      "tflops": round(kflop[n] / (t * 1e-3) / 1e12, 2)}
+    dom = max((n for n in names if n != "rowterm"), key=lambda n: per[n].mean())
+    dom_t = float(per[dom].mean())
+    achieved = kflop[dom] / (dom_t * 1e-3) / 1e12
     traffic = None
     if os.path.exists(PROFILE_TRAFFIC):
-        rec = json.load(open(PROFILE_TRAFFIC)).get(w.name, {}).get("fwd")
-        digest = source_digest("io_aware_exact_10_amd/csrc/fa_fwd_bf16.hip", "io_aware_exact_10_amd/csrc/fa_common.h")
-        if rec and rec.get("source_digest") == digest:
+        rec = json.load(open(PROFILE_TRAFFIC)).get(w.name, {}).get(dom)
+        if rec and rec.get("source_digest") == source_digest(*KERNEL_SOURCES[dom]):
             traffic = rec.get("hbm_bytes_per_launch")
-    roofline = {"kernel": "fwd_bf16_kernel" if w.dtype == synth.DTYPE_BF16 else "fwd_f32_kernel",
+    roofline = {"kernel": KERNEL_NAMES[dom],
                 "bound": "mfma" if w.dtype == synth.DTYPE_BF16 else "alu",
-                "achieved": round(fwd_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-                "frac": round(fwd_tflops / peak, 4), "traffic": traffic,
-                "flop_per_launch": fwd_flop, "mean_launch_ms": round(float(fwd_ms.mean()), 4)}
+                "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "flop_per_launch": kflop[dom], "mean_launch_ms": round(dom_t, 4)}
 
     naive = None
     if not args.no_naive and w.N <= 4096:
@@ -230,6 +335,14 @@ def main() -> int:
         except Exception as ex:  # noqa: BLE001
             naive = {"error": repr(ex)[:200]}
         torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -260,6 +373,7 @@ def main() -> int:
                 "frac": round(fwd_tflops / peak, 4), "gflop": round(fwd_flop / 1e9, 2)},
         "bwd": ({"ms": round(float(bwd_ms.mean()), 4), "tflops": round(bwd_tflops, 2),
                  "frac": round(bwd_tflops / peak, 4), "gflop": round(bwd_flop / 1e9, 2)} if backward else None),
+        "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "naive": naive,

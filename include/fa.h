@@ -114,6 +114,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int mask_kind, const uint8_t* block_mask, int dtype,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * The three steps fa_bwd enqueues, callable one by one with the same
+ * arguments and the same validation (arguments a step does not use are not
+ * taken). fa_bwd_rowterm writes the row term D into the workspace;
+ * fa_bwd_dkdv and fa_bwd_dq each read it and are independent of each other,
+ * so they may run on two streams once the row term is complete.
+ * workspace has the size and alignment fa_bwd requires; for fa_bwd_dkdv and
+ * fa_bwd_dq its contents must be those fa_bwd_rowterm left.
+ */
+int fa_bwd_rowterm(const void* o, const void* dO, int B, int H, int N, int d, int dtype,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                void* dk, void* dv, int B, int H, int N, int d, float scale,
+                int mask_kind, const uint8_t* block_mask, int dtype,
+                const void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+              void* dq, int B, int H, int N, int d, float scale,
+              int mask_kind, const uint8_t* block_mask, int dtype,
+              const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a fa_status value ("unknown status" otherwise). */
 const char* fa_status_string(int status);
 

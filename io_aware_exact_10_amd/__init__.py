@@ -25,7 +25,8 @@ __all__ = [
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_MASK",
     "FA_ERR_WORKSPACE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_ARG",
     "MASK_NONE", "MASK_CAUSAL", "MASK_BLOCK_SPARSE", "DTYPE_BF16", "DTYPE_F32",
-    "FAError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string",
+    "FAError", "fa_fwd", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
+    "fa_bwd_workspace_bytes", "fa_status_string",
     "forward", "backward", "library_path", "lib",
 ]
 
@@ -68,6 +69,12 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd.restype = i
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
         L.fa_bwd.restype = i
+        L.fa_bwd_rowterm.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+        L.fa_bwd_rowterm.restype = i
+        L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+        L.fa_bwd_dkdv.restype = i
+        L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+        L.fa_bwd_dq.restype = i
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
         L.fa_bwd_workspace_bytes.restype = sz
         L.fa_status_string.argtypes = [i]
@@ -103,6 +110,22 @@ def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, mask_kind, block_
            workspace, workspace_bytes, stream) -> int:
     return int(lib().fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, ctypes.c_float(scale),
                             mask_kind, block_mask, dtype, workspace, workspace_bytes, stream))
+
+
+def fa_bwd_rowterm(o, dO, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
+    return int(lib().fa_bwd_rowterm(o, dO, B, H, N, d, dtype, workspace, workspace_bytes, stream))
+
+
+def fa_bwd_dkdv(q, k, v, lse, dO, dk, dv, B, H, N, d, scale, mask_kind, block_mask, dtype,
+                workspace, workspace_bytes, stream) -> int:
+    return int(lib().fa_bwd_dkdv(q, k, v, lse, dO, dk, dv, B, H, N, d, ctypes.c_float(scale), mask_kind,
+                                 block_mask, dtype, workspace, workspace_bytes, stream))
+
+
+def fa_bwd_dq(q, k, v, lse, dO, dq, B, H, N, d, scale, mask_kind, block_mask, dtype,
+              workspace, workspace_bytes, stream) -> int:
+    return int(lib().fa_bwd_dq(q, k, v, lse, dO, dq, B, H, N, d, ctypes.c_float(scale), mask_kind,
+                               block_mask, dtype, workspace, workspace_bytes, stream))
 
 
 # ---------------------------------------------------------------------------
@@ -162,8 +185,14 @@ def forward(q, k, v, scale=None, mask_kind=MASK_NONE, block_mask=None, out=None,
 
 
 def backward(q, k, v, o, lse, do, scale=None, mask_kind=MASK_NONE, block_mask=None,
-             workspace=None, dq=None, dk=None, dv=None):
-    """Attention backward on the current stream; returns (dq, dk, dv)."""
+             workspace=None, dq=None, dk=None, dv=None, steps="all"):
+    """Attention backward on the current stream; returns (dq, dk, dv).
+
+    ``steps`` selects what is enqueued: "all" (fa_bwd), or one of "rowterm",
+    "dkdv", "dq" (the three steps of fa_bwd, for callers that time or
+    schedule them separately; "dkdv" and "dq" need the workspace a previous
+    "rowterm" call filled).
+    """
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     for t in (o, do):
@@ -179,10 +208,24 @@ def backward(q, k, v, o, lse, do, scale=None, mask_kind=MASK_NONE, block_mask=No
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     mp = _mask_ptr(mask_kind, block_mask, N, q.device)
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, mask_kind, mp,
-                _DT[q.dtype], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                _stream(q.device))
+    wsb = workspace.numel() * workspace.element_size()
+    dt = _DT[q.dtype]
+    stream = _stream(q.device)
+    if steps == "all":
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, mask_kind, mp,
+                    dt, workspace.data_ptr(), wsb, stream)
+    elif steps == "rowterm":
+        st = fa_bwd_rowterm(o.data_ptr(), do.data_ptr(), B, H, N, d, dt, workspace.data_ptr(), wsb, stream)
+    elif steps == "dkdv":
+        st = fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                         dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, mask_kind, mp, dt,
+                         workspace.data_ptr(), wsb, stream)
+    elif steps == "dq":
+        st = fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                       dq.data_ptr(), B, H, N, d, scale, mask_kind, mp, dt, workspace.data_ptr(), wsb, stream)
+    else:
+        raise ValueError(f"unknown steps {steps!r}")
     if st != FA_OK:
-        raise FAError(st, "fa_bwd")
+        raise FAError(st, f"fa_bwd ({steps})")
     return dq, dk, dv

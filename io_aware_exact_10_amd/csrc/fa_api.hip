@@ -102,46 +102,109 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return e == 0 ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-           const void* dO, void* dq, void* dk, void* dv,
-           int B, int H, int N, int d, float scale,
-           int mask_kind, const uint8_t* block_mask, int dtype,
-           void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// Validation shared by fa_bwd and its three steps. Pointers a step does not
+// use are passed as `unused` and skipped; every used pointer must be non-NULL
+// and aligned, and no output may overlap an input or another output.
+const char kUnusedTag = 0;
+const void* const unused = &kUnusedTag;
+
+int bwd_prepare(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, const void* dq, const void* dk, const void* dv,
+                int B, int H, int N, int d, float scale, int mask_kind, const uint8_t* block_mask,
+                int dtype, const void* workspace, size_t workspace_bytes, fa::AttnParams* out) {
+  const void* tens[8] = {q, k, v, o, dO, dq, dk, dv};
+  for (const void* t : tens)
+    if (!t) return FA_ERR_NULL;
+  if (!lse) return FA_ERR_NULL;
   int64_t elems = 0;
   int st = check_common(B, H, N, d, scale, mask_kind, block_mask, dtype, &elems);
   if (st != FA_OK) return st;
   const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
-      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(workspace, 16))
-    return FA_ERR_ALIGN;
+  for (const void* t : tens)
+    if (t != unused && !aligned(t, 16)) return FA_ERR_ALIGN;
+  if ((const void*)lse != unused && !aligned(lse, 4)) return FA_ERR_ALIGN;
+  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
   const size_t tb = (size_t)elems * (dtype == FA_BF16 ? 2 : 4);
   const size_t lb = (size_t)B * H * N * sizeof(float);
   const void* ins[6] = {q, k, v, o, dO, lse};
   const size_t insz[6] = {tb, tb, tb, tb, tb, lb};
-  void* outs[4] = {dq, dk, dv, workspace};
+  const void* outs[4] = {dq, dk, dv, workspace};
   const size_t outsz[4] = {tb, tb, tb, need};
   for (int i = 0; i < 4; ++i) {
+    if (outs[i] == unused) continue;
     for (int j = 0; j < 6; ++j)
-      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ARG;
+      if (ins[j] != unused && overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ARG;
     for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ARG;
+      if (outs[j] != unused && overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ARG;
   }
   fa::AttnParams p = make_params(B, H, N, d, scale, mask_kind, block_mask);
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = const_cast<void*>(o);
-  p.lse = const_cast<float*>(lse);
-  p.dO = dO;
-  p.dq = dq;
-  p.dk = dk;
-  p.dv = dv;
-  p.dterm = (float*)workspace;
-  const int e = dtype == FA_BF16 ? fa::launch_bwd_bf16(p, mask_kind, stream)
-                                 : fa::launch_bwd_f32(p, mask_kind, stream);
+  auto take = [](const void* x) -> const void* { return x == unused ? nullptr : x; };
+  p.q = take(q);
+  p.k = take(k);
+  p.v = take(v);
+  p.o = const_cast<void*>(take(o));
+  p.lse = const_cast<float*>((const float*)take(lse));
+  p.dO = take(dO);
+  p.dq = const_cast<void*>(take(dq));
+  p.dk = const_cast<void*>(take(dk));
+  p.dv = const_cast<void*>(take(dv));
+  p.dterm = (float*)const_cast<void*>(workspace);
+  *out = p;
+  return FA_OK;
+}
+
+int bwd_launch(const fa::AttnParams& p, int mask_kind, int dtype, int steps, hipStream_t stream) {
+  const int e = dtype == FA_BF16 ? fa::launch_bwd_bf16(p, mask_kind, steps, stream)
+                                 : fa::launch_bwd_f32(p, mask_kind, steps, stream);
   return e == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale,
+           int mask_kind, const uint8_t* block_mask, int dtype,
+           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fa::AttnParams p;
+  const int st = bwd_prepare(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, mask_kind, block_mask,
+                             dtype, workspace, workspace_bytes, &p);
+  return st != FA_OK ? st : bwd_launch(p, mask_kind, dtype, fa::kBwdAll, stream);
+}
+
+int fa_bwd_rowterm(const void* o, const void* dO, int B, int H, int N, int d, int dtype,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fa::AttnParams p;
+  const int st = bwd_prepare(unused, unused, unused, o, (const float*)unused, dO, unused, unused, unused,
+                             B, H, N, d, 1.0f, FA_MASK_NONE, nullptr, dtype, workspace, workspace_bytes, &p);
+  return st != FA_OK ? st : bwd_launch(p, FA_MASK_NONE, dtype, fa::kBwdRowterm, stream);
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                void* dk, void* dv, int B, int H, int N, int d, float scale,
+                int mask_kind, const uint8_t* block_mask, int dtype,
+                const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fa::AttnParams p;
+  const int st = bwd_prepare(q, k, v, unused, lse, dO, unused, dk, dv, B, H, N, d, scale, mask_kind, block_mask,
+                             dtype, workspace, workspace_bytes, &p);
+  return st != FA_OK ? st : bwd_launch(p, mask_kind, dtype, fa::kBwdDkdv, stream);
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+              void* dq, int B, int H, int N, int d, float scale,
+              int mask_kind, const uint8_t* block_mask, int dtype,
+              const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fa::AttnParams p;
+  const int st = bwd_prepare(q, k, v, unused, lse, dO, dq, unused, unused, B, H, N, d, scale, mask_kind, block_mask,
+                             dtype, workspace, workspace_bytes, &p);
+  return st != FA_OK ? st : bwd_launch(p, mask_kind, dtype, fa::kBwdDq, stream);
 }
 
 }  // extern "C"

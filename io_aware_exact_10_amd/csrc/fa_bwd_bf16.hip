@@ -386,10 +386,10 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 // launchers
 // ---------------------------------------------------------------------------
 template <int D, int MASK>
-static int launch_bwd_t(const AttnParams& p, hipStream_t stream) {
+static int launch_bwd_t(const AttnParams& p, int steps, hipStream_t stream) {
   AttnParams pp = p;
   const size_t rows = (size_t)p.B * p.H * p.N;
-  {
+  if (steps & kBwdRowterm) {
     const size_t threads = rows * (D / 8);
     const uint32_t grid = (uint32_t)((threads + kThreads - 1) / kThreads);
     size_t rr = rows;
@@ -398,7 +398,7 @@ static int launch_bwd_t(const AttnParams& p, hipStream_t stream) {
                                    args, 0, stream);
     if (e != hipSuccess) return (int)e;
   }
-  {
+  if (steps & kBwdDkdv) {
     uint32_t nkt = (uint32_t)((p.N + kDkvBK - 1) / kDkvBK);
     uint32_t total = nkt * (uint32_t)p.B * (uint32_t)p.H;
     void* args[] = {&pp, &nkt, &total};
@@ -406,7 +406,7 @@ static int launch_bwd_t(const AttnParams& p, hipStream_t stream) {
                                    args, 0, stream);
     if (e != hipSuccess) return (int)e;
   }
-  {
+  if (steps & kBwdDq) {
     uint32_t nqt = (uint32_t)((p.N + kDqBQ - 1) / kDqBQ);
     uint32_t total = nqt * (uint32_t)p.B * (uint32_t)p.H;
     void* args[] = {&pp, &nqt, &total};
@@ -417,15 +417,15 @@ static int launch_bwd_t(const AttnParams& p, hipStream_t stream) {
   return 0;
 }
 
-int launch_bwd_bf16(const AttnParams& p, int mask_kind, hipStream_t stream) {
+int launch_bwd_bf16(const AttnParams& p, int mask_kind, int steps, hipStream_t stream) {
   if (p.d == 64) {
-    if (mask_kind == 0) return launch_bwd_t<64, 0>(p, stream);
-    if (mask_kind == 1) return launch_bwd_t<64, 1>(p, stream);
-    return launch_bwd_t<64, 2>(p, stream);
+    if (mask_kind == 0) return launch_bwd_t<64, 0>(p, steps, stream);
+    if (mask_kind == 1) return launch_bwd_t<64, 1>(p, steps, stream);
+    return launch_bwd_t<64, 2>(p, steps, stream);
   }
-  if (mask_kind == 0) return launch_bwd_t<128, 0>(p, stream);
-  if (mask_kind == 1) return launch_bwd_t<128, 1>(p, stream);
-  return launch_bwd_t<128, 2>(p, stream);
+  if (mask_kind == 0) return launch_bwd_t<128, 0>(p, steps, stream);
+  if (mask_kind == 1) return launch_bwd_t<128, 1>(p, steps, stream);
+  return launch_bwd_t<128, 2>(p, steps, stream);
 }
 
 }  // namespace fa

@@ -283,10 +283,10 @@ static int launch_fwd_f32_t(const AttnParams& p, hipStream_t stream) {
 }
 
 template <int D, int MASK>
-static int launch_bwd_f32_t(const AttnParams& p, hipStream_t stream) {
+static int launch_bwd_f32_t(const AttnParams& p, int steps, hipStream_t stream) {
   constexpr int ROWS = kF32Threads / (D / 32);
   AttnParams pp = p;
-  {
+  if (steps & kBwdRowterm) {
     size_t rows = (size_t)p.B * p.H * p.N;
     const uint32_t grid = (uint32_t)((rows * (D / 32) + kF32Threads - 1) / kF32Threads);
     void* args[] = {&pp, &rows};
@@ -295,12 +295,12 @@ static int launch_bwd_f32_t(const AttnParams& p, hipStream_t stream) {
   }
   uint32_t nt = (uint32_t)((p.N + ROWS - 1) / ROWS);
   uint32_t total = nt * (uint32_t)p.B * (uint32_t)p.H;
-  {
+  if (steps & kBwdDkdv) {
     void* args[] = {&pp, &nt, &total};
     hipError_t e = hipLaunchKernel((const void*)&bwd_dkdv_f32_kernel<D, MASK>, dim3(total), dim3(kF32Threads), args, 0, stream);
     if (e != hipSuccess) return (int)e;
   }
-  {
+  if (steps & kBwdDq) {
     void* args[] = {&pp, &nt, &total};
     hipError_t e = hipLaunchKernel((const void*)&bwd_dq_f32_kernel<D, MASK>, dim3(total), dim3(kF32Threads), args, 0, stream);
     if (e != hipSuccess) return (int)e;
@@ -319,15 +319,15 @@ int launch_fwd_f32(const AttnParams& p, int mask_kind, hipStream_t stream) {
   return launch_fwd_f32_t<128, 2>(p, stream);
 }
 
-int launch_bwd_f32(const AttnParams& p, int mask_kind, hipStream_t stream) {
+int launch_bwd_f32(const AttnParams& p, int mask_kind, int steps, hipStream_t stream) {
   if (p.d == 64) {
-    if (mask_kind == 0) return launch_bwd_f32_t<64, 0>(p, stream);
-    if (mask_kind == 1) return launch_bwd_f32_t<64, 1>(p, stream);
-    return launch_bwd_f32_t<64, 2>(p, stream);
+    if (mask_kind == 0) return launch_bwd_f32_t<64, 0>(p, steps, stream);
+    if (mask_kind == 1) return launch_bwd_f32_t<64, 1>(p, steps, stream);
+    return launch_bwd_f32_t<64, 2>(p, steps, stream);
   }
-  if (mask_kind == 0) return launch_bwd_f32_t<128, 0>(p, stream);
-  if (mask_kind == 1) return launch_bwd_f32_t<128, 1>(p, stream);
-  return launch_bwd_f32_t<128, 2>(p, stream);
+  if (mask_kind == 0) return launch_bwd_f32_t<128, 0>(p, steps, stream);
+  if (mask_kind == 1) return launch_bwd_f32_t<128, 1>(p, steps, stream);
+  return launch_bwd_f32_t<128, 2>(p, steps, stream);
 }
 
 }  // namespace fa

@@ -27,9 +27,13 @@ struct AttnParams {
 };
 
 // Each returns a hipError_t value (0 on success).
+// The backward is three launches: the row term, then dK/dV and dQ (these two
+// depend only on the row term).
+enum BwdStep { kBwdRowterm = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7 };
+
 int launch_fwd_bf16(const AttnParams& p, int mask_kind, hipStream_t stream);
-int launch_bwd_bf16(const AttnParams& p, int mask_kind, hipStream_t stream);
+int launch_bwd_bf16(const AttnParams& p, int mask_kind, int steps, hipStream_t stream);
 int launch_fwd_f32(const AttnParams& p, int mask_kind, hipStream_t stream);
-int launch_bwd_f32(const AttnParams& p, int mask_kind, hipStream_t stream);
+int launch_bwd_f32(const AttnParams& p, int mask_kind, int steps, hipStream_t stream);
 
 }  // namespace fa

@@ -46,7 +46,8 @@ def call_bwd(**kw):
 
 def test_library_exports_every_declared_symbol():
     names = fa.declared_functions()
-    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string"}
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
+                          "fa_bwd_workspace_bytes", "fa_status_string"}
     L = fa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -142,3 +143,41 @@ def test_product_path_does_not_reference_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 txt = open(os.path.join(root, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
+
+
+def step_args(name, **kw):
+    a = bwd_args()
+    if name == "rowterm":
+        keep = ["o", "dO", "B", "H", "N", "d", "dtype", "workspace", "workspace_bytes", "stream"]
+    elif name == "dkdv":
+        keep = ["q", "k", "v", "lse", "dO", "dk", "dv", "B", "H", "N", "d", "scale", "mask_kind",
+                "block_mask", "dtype", "workspace", "workspace_bytes", "stream"]
+    else:
+        keep = ["q", "k", "v", "lse", "dO", "dq", "B", "H", "N", "d", "scale", "mask_kind",
+                "block_mask", "dtype", "workspace", "workspace_bytes", "stream"]
+    a = {k: a[k] for k in keep}
+    a.update(kw)
+    return a
+
+
+STEPS = {"rowterm": fa.fa_bwd_rowterm, "dkdv": fa.fa_bwd_dkdv, "dq": fa.fa_bwd_dq}
+
+
+@pytest.mark.parametrize("name", ["rowterm", "dkdv", "dq"])
+def test_bwd_step_validation(name):
+    f = STEPS[name]
+    first = {"rowterm": "o", "dkdv": "q", "dq": "q"}[name]
+    assert f(**step_args(name, **{first: None})) == fa.FA_ERR_NULL
+    assert f(**step_args(name, d=96)) == fa.FA_ERR_UNSUPPORTED
+    assert f(**step_args(name, N=0)) == fa.FA_ERR_SHAPE
+    assert f(**step_args(name, workspace=None)) == fa.FA_ERR_WORKSPACE
+    assert f(**step_args(name, workspace_bytes=8)) == fa.FA_ERR_WORKSPACE
+    assert f(**step_args(name, workspace=9 * BIG + A + 4)) == fa.FA_ERR_ALIGN
+    if name != "rowterm":
+        assert f(**step_args(name, mask_kind=2, block_mask=None)) == fa.FA_ERR_MASK
+        assert f(**step_args(name, scale=math.nan)) == fa.FA_ERR_ARG
+        out = "dk" if name == "dkdv" else "dq"
+        assert f(**step_args(name, **{out: A})) == fa.FA_ERR_ARG          # output aliases q
+        assert f(**step_args(name, lse=4 * BIG + A + 1)) == fa.FA_ERR_ALIGN
+    else:
+        assert f(**step_args(name, workspace=A + 3 * BIG)) == fa.FA_ERR_ARG   # workspace aliases o
