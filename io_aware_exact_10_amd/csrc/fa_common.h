@@ -136,6 +136,34 @@ __device__ __forceinline__ u32x4 tile_col_frag(const uint8_t* tile, int row0, in
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
+// Cheap fragment addressing for swizzled tiles. The swizzle only XORs the
+// chunk field (bits 4..7 of the byte offset within a 2D-byte row), so for
+// rows row0 = multiple of 16 and column blocks col0 = 32 dt:
+//   tile_off(row0 + r, 16 ks + 8 h) = row0 * 2D + (row_base ^ 32 ks)
+//   tile_off(row0 + 8 sel + rl, 32 dt + c) = row0 * 2D + (col_base[sel] ^ 64 dt)
+// with per-lane bases that do not change inside the kernel. One XOR per
+// fragment (none for ks = 0 / dt = 0); row0 * 2D is a constant offset.
+template <int D>
+__device__ __forceinline__ int row_frag_base(int lane) {
+  return tile_off<D>(lane & 31, 8 * (lane >> 5));
+}
+template <int D>
+__device__ __forceinline__ int col_frag_base(int lane, int sel) {
+  const int g = lane >> 4, jj = (lane >> 2) & 3, q = lane & 3;
+  return tile_off<D>(8 * sel + 4 * (g >> 1) + jj, 16 * (g & 1) + 4 * q);
+}
+// Row operand (lane: row row0 + lane % 32, elements [16 ks + 8 h, +8)).
+__device__ __forceinline__ u32x4 row_frag(const uint8_t* tile_row0, int base, int ks) {
+  return *(const u32x4*)(tile_row0 + (base ^ (32 * ks)));
+}
+// Column operand (the tile transposed), same slots as tile_col_frag.
+__device__ __forceinline__ u32x4 col_frag(const uint8_t* tile_row0, int base0, int base1, int dt) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_row0 + (base0 ^ (64 * dt))));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_row0 + (base1 ^ (64 * dt))));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
 // Workgroup id -> logical tile id so that consecutive logical tiles (the query
 // tiles of one head) run on the same XCD and share its L2. Hardware hands out
 // workgroup ids round-robin over the 8 XCDs; this maps XCD x to the contiguous

@@ -28,6 +28,8 @@
 //                   bf16), A = V^T read from the row-major V tile with LDS
 //                   transpose reads, in the key order P^T occupies.
 // Epilogue: O = acc / l, LSE = ln 2 * (m + log2 l).
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -47,7 +49,7 @@ struct alignas(16) FwdSmem {
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 template <int D, int MASK>
-__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
+__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3))) void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   __shared__ FwdSmem<D> sm;
   constexpr int TPB = kMaskBlock / kFwdBC;                 // key tiles per mask block
   constexpr int NDT = D / 32;                              // 32-row blocks of O^T
@@ -85,6 +87,8 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     tile_load_async<D, kFwdBC, 4>(sm.k[buf], Kh, kt * kFwdBC, N, w, lane);
     tile_load_async<D, kFwdBC, 4>(sm.v[buf], Vh, kt * kFwdBC, N, w, lane);
   };
+  const int kbase_l = row_frag_base<D>(lane);
+  const int vbase0_l = col_frag_base<D>(lane, 0), vbase1_l = col_frag_base<D>(lane, 1);
 
   int kt = next_tile(0);
   if (kt < kend) issue(kt, 0);
@@ -105,48 +109,59 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2))
   float l_run = 0.f;         // this lane's partial running sum (its 16-key half)
   const float c = p.c;
 
-  auto compute = [&](int buf, int kt) {
+  // One key tile in stages over its two 32-key sub-blocks, ordered so the
+  // MFMA pipe and the VALU have independent work side by side:
+  //   S0 | S1 with the masking and row max of S0 | max of S1, rescale
+  //   decision | exp of S0 | PV0 with exp of S1 | PV1.
+  // Operand fragments of a sub-block are read from LDS as a batch before its
+  // products. NM selects the masked variant (diagonal and tail tiles only).
+  auto tile = [&](int buf, int kt, auto nm) {
+    constexpr bool NM = decltype(nm)::value;
     const int k0 = kt * kFwdBC;
-    if (MASK == 1 && k0 > qw0 + 31) return;      // whole tile above this wave's diagonal
-    const bool need_mask = (k0 + kFwdBC > N) || (MASK == 1 && k0 + kFwdBC - 1 > qw0);
-    bool live[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) live[kb] = !(MASK == 1 && k0 + kb * 32 > qw0 + 31);
+    const uint8_t* kt_ = sm.k[buf];
+    const uint8_t* vt_ = sm.v[buf];
+    const bool live1 = !(MASK == 1 && k0 + 32 > qw0 + 31);
+    // Opaque copies of the per-lane bases: the compiler recomputes the few
+    // XORed fragment addresses here instead of keeping all of them live
+    // across the loop (which would cost 16 VGPRs).
+    int kbase = kbase_l, vbase0 = vbase0_l, vbase1 = vbase1_l;
+    asm volatile("" : "+v"(kbase), "+v"(vbase0), "+v"(vbase1));
 
-    f32x16 s[2];
+    u32x4 kf[D / 16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
-      if (live[kb]) {
+    for (int ks = 0; ks < D / 16; ++ks) kf[ks] = row_frag(kt_, kbase, ks);
+    f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          s[kb] = mfma_32x32x16(tile_row_frag<D>(sm.k[buf], kb * 32, r, h, ks), qf[ks], s[kb]);
+    for (int ks = 0; ks < D / 16; ++ks) s0 = mfma_32x32x16(kf[ks], qf[ks], s0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (live1) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) kf[ks] = row_frag(kt_ + 32 * 2 * D, kbase, ks);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) s1 = mfma_32x32x16(kf[ks], qf[ks], s1);
+    }
+    // Scores of a sub-block to the exp2 domain: masked entries -inf.
+    auto scale_mask = [&](f32x16& sv, int kb, bool live) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        const bool vis = live && key < N && (MASK != 1 || key <= qi);
+        sv[i] = vis ? sv[i] * c : -INFINITY;
       }
+    };
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+    if (NM) scale_mask(s0, 0, true);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx0 = fmaxf(mx0, s0[i]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (NM) scale_mask(s1, 1, live1);
+    if (live1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx1 = fmaxf(mx1, s1[i]);
     }
-
-    // Scores to the exp2 domain (masked entries -inf) and the tile row max.
-    float mx;
-    if (!need_mask) {
-      mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-    } else {
-      mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          const bool vis = live[kb] && key < N && (MASK != 1 || key <= qi);
-          const float t = vis ? s[kb][i] * c : -INFINITY;
-          s[kb][i] = t;
-          mx = fmaxf(mx, t);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-    }
+    float mx = fmaxf(mx0, mx1);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (!NM) mx *= c;
     // Raise the reference max only when some row of the wave outgrows it.
     if (__ballot(mx > m_run + kRescaleThreshold)) {
       const float m_new = fmaxf(m_run, mx);
@@ -159,36 +174,52 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-
-    // P^T as the B operand: registers 8st..8st+7 of sub-block kb form k-step st.
-    u32x4 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    // p = 2^(t - m) packed to bf16 as the P^T B operand (k-steps st = 0, 1);
+    // the fp32 row sum uses the unrounded p.
+    auto expo = [&](const f32x16& sv, u32x4 pb[2]) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float sv = s[kb][8 * st + e];
-          x[e] = need_mask ? fast_exp2(sv - m_use) : fast_exp2(__builtin_fmaf(sv, c, -m_use));
+          const float t = sv[8 * st + e];
+          x[e] = NM ? fast_exp2(t - m_use) : fast_exp2(__builtin_fmaf(t, c, -m_use));
+          l_run += x[e];
         }
-        pb[kb][st] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                           pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
-        // fp32 row sum of the unrounded p: the log-sum-exp must not carry the
-        // bf16 rounding of P.
-#pragma unroll
-        for (int e = 0; e < 8; ++e) l_run += x[e];
+        pb[st] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
       }
+    };
+    auto pv = [&](int kb, const u32x4 pb[2]) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt) {
+        u32x4 vf[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (!live[kb]) continue;
+        for (int st = 0; st < 2; ++st) vf[st] = col_frag(vt_ + (kb * 32 + st * 16) * 2 * D, vbase0, vbase1, dt);
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-          acc[dt] = mfma_32x32x16(tile_col_frag<D>(sm.v[buf], kb * 32 + st * 16, dt * 32, lane), pb[kb][st],
-                                  acc[dt]);
+        for (int st = 0; st < 2; ++st) acc[dt] = mfma_32x32x16(vf[st], pb[st], acc[dt]);
       }
+    };
+    u32x4 pb0[2], pb1[2];
+    expo(s0, pb0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (live1) {
+      pv(0, pb0);
+      expo(s1, pb1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(1, pb1);
+    } else {
+      pv(0, pb0);
+    }
+  };
+  auto compute = [&](int buf, int kt) {
+    const int k0 = kt * kFwdBC;
+    if (MASK == 1 && k0 > qw0 + 31) return;      // whole tile above this wave's diagonal
+    const bool need_mask = (k0 + kFwdBC > N) || (MASK == 1 && k0 + kFwdBC - 1 > qw0);
+    if (need_mask)
+      tile(buf, kt, std::true_type{});
+    else
+      tile(buf, kt, std::false_type{});
   };
 
   wait_vmem();
