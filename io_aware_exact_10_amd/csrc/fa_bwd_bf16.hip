@@ -150,9 +150,19 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     dvT[i] = zero16();
   }
   const float c = p.c;
+  const int rbase_l = row_frag_base<D>(lane);
+  const int cbase0_l = col_frag_base<D>(lane, 0), cbase1_l = col_frag_base<D>(lane, 1);
 
   auto compute = [&](int buf, int it) {
     const int q0 = it * kDkvBQ;
+    // Per-tile lane addresses relative to the shared block (see the
+    // forward kernel): one XOR per fragment, opaque so they are not all
+    // kept live across the loop.
+    const uint8_t* sbase = (const uint8_t*)&sm;
+    const int oq = (int)(sm.q[buf] - sbase), oo = (int)(sm.dO[buf] - sbase);
+    int qr = rbase_l + oq, orow = rbase_l + oo;
+    int qc0 = cbase0_l + oq, qc1 = cbase1_l + oq, oc0 = cbase0_l + oo, oc1 = cbase1_l + oo;
+    asm volatile("" : "+v"(qr), "+v"(orow), "+v"(qc0), "+v"(qc1), "+v"(oc0), "+v"(oc1));
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int qb0 = q0 + 32 * mb;
@@ -161,10 +171,10 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        s = mfma_32x32x16(tile_row_frag<D>(sm.q[buf], mb * 32, r, h, ks), kf[ks], s);
+        s = mfma_32x32x16(row_frag(sbase + mb * 32 * 2 * D, qr, ks), kf[ks], s);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        dp = mfma_32x32x16(tile_row_frag<D>(sm.dO[buf], mb * 32, r, h, ks), vf[ks], dp);
+        dp = mfma_32x32x16(row_frag(sbase + mb * 32 * 2 * D, orow, ks), vf[ks], dp);
       u32x4 pb[2], db[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -198,8 +208,9 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          dvT[dt] = mfma_32x32x16(tile_col_frag<D>(sm.dO[buf], mb * 32 + st * 16, dt * 32, lane), pb[st], dvT[dt]);
-          dkT[dt] = mfma_32x32x16(tile_col_frag<D>(sm.q[buf], mb * 32 + st * 16, dt * 32, lane), db[st], dkT[dt]);
+          const uint8_t* rowp = sbase + (mb * 32 + st * 16) * 2 * D;
+          dvT[dt] = mfma_32x32x16(col_frag(rowp, oc0, oc1, dt), pb[st], dvT[dt]);
+          dkT[dt] = mfma_32x32x16(col_frag(rowp, qc0, qc1, dt), db[st], dkT[dt]);
         }
     }
   };
@@ -314,10 +325,16 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 #pragma unroll
   for (int i = 0; i < NDT; ++i) dqT[i] = zero16();
   const float c = p.c;
+  const int rbase_l = row_frag_base<D>(lane);
+  const int cbase0_l = col_frag_base<D>(lane, 0), cbase1_l = col_frag_base<D>(lane, 1);
 
   auto compute = [&](int buf, int kt) {
     const int k0 = kt * kDqBK;
     if (MASK == 1 && k0 > qw0 + 31) return;
+    const uint8_t* sbase = (const uint8_t*)&sm;
+    const int ok = (int)(sm.k[buf] - sbase), ov = (int)(sm.v[buf] - sbase);
+    int kr = rbase_l + ok, vr = rbase_l + ov, kc0 = cbase0_l + ok, kc1 = cbase1_l + ok;
+    asm volatile("" : "+v"(kr), "+v"(vr), "+v"(kc0), "+v"(kc1));
     const bool need_mask = (k0 + kDqBK > N) || (MASK == 1 && k0 + kDqBK - 1 > qw0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -325,10 +342,10 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        s = mfma_32x32x16(tile_row_frag<D>(sm.k[buf], kb * 32, r, h, ks), qf[ks], s);
+        s = mfma_32x32x16(row_frag(sbase + kb * 32 * 2 * D, kr, ks), qf[ks], s);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        dp = mfma_32x32x16(tile_row_frag<D>(sm.v[buf], kb * 32, r, h, ks), of[ks], dp);
+        dp = mfma_32x32x16(row_frag(sbase + kb * 32 * 2 * D, vr, ks), of[ks], dp);
       u32x4 db[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -350,7 +367,7 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
-          dqT[dt] = mfma_32x32x16(tile_col_frag<D>(sm.k[buf], kb * 32 + st * 16, dt * 32, lane), db[st], dqT[dt]);
+          dqT[dt] = mfma_32x32x16(col_frag(sbase + (kb * 32 + st * 16) * 2 * D, kc0, kc1, dt), db[st], dqT[dt]);
     }
   };
 

@@ -40,10 +40,12 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// Two floats -> two bf16 (round to nearest even) packed low|high.
+// Two floats -> two bf16 (round to nearest even) packed low|high: a single
+// two-source v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
@@ -111,31 +113,6 @@ __device__ __forceinline__ void tile_load_async(uint8_t* tile, const uint16_t* _
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// A operand taken along the rows of a swizzled tile: lane (r = l % 32,
-// h = l / 32) gets row row0 + r, elements [16 ks + 8 h, +8).
-template <int D>
-__device__ __forceinline__ u32x4 tile_row_frag(const uint8_t* tile, int row0, int r, int h, int ks) {
-  return *(const u32x4*)(tile + tile_off<D>(row0 + r, ks * 16 + h * 8));
-}
-
-// A operand taken down the columns of a swizzled tile (the tile transposed):
-// lane (m = l % 32, h = l / 32) gets column col0 + m at the 8 rows
-// row0 + {4h..4h+3, 8+4h..8+4h+3}, the contraction slots a B operand built
-// from an MFMA C layout occupies. Two transpose reads: within each 16-lane
-// group, lane i receives element i % 4 of the 8-byte chunks addressed by
-// lanes 4 j + i / 4 (j = 0..3), so lane s of group g addresses row
-// row0 + 8 sel + 4 (g / 2) + (s % 16) / 4, columns col0 + 16 (g % 2) + 4 (s % 4).
-template <int D>
-__device__ __forceinline__ u32x4 tile_col_frag(const uint8_t* tile, int row0, int col0, int lane) {
-  const int g = lane >> 4, jj = (lane >> 2) & 3, q = lane & 3;
-  const int rl = 4 * (g >> 1) + jj;
-  const int cl = col0 + 16 * (g & 1) + 4 * q;
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off<D>(row0 + rl, cl)));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off<D>(row0 + 8 + rl, cl)));
-  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
-  return u32x4{ua[0], ua[1], ub[0], ub[1]};
-}
-
 // Cheap fragment addressing for swizzled tiles. The swizzle only XORs the
 // chunk field (bits 4..7 of the byte offset within a 2D-byte row), so for
 // rows row0 = multiple of 16 and column blocks col0 = 32 dt:
@@ -156,7 +133,13 @@ __device__ __forceinline__ int col_frag_base(int lane, int sel) {
 __device__ __forceinline__ u32x4 row_frag(const uint8_t* tile_row0, int base, int ks) {
   return *(const u32x4*)(tile_row0 + (base ^ (32 * ks)));
 }
-// Column operand (the tile transposed), same slots as tile_col_frag.
+// Column operand (the tile transposed): lane (m = l % 32, h = l / 32) gets
+// column m of the block at the 8 rows {4h..4h+3, 8+4h..8+4h+3}, the
+// contraction slots a B operand built from an MFMA C layout occupies. Two
+// transpose reads: within each 16-lane group, lane i receives element i % 4
+// of the 8-byte chunks addressed by lanes 4 j + i / 4 (j = 0..3), so lane s
+// of group g addresses row 8 sel + 4 (g / 2) + (s % 16) / 4, columns
+// 16 (g % 2) + 4 (s % 4) (col_frag_base).
 __device__ __forceinline__ u32x4 col_frag(const uint8_t* tile_row0, int base0, int base1, int dt) {
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_row0 + (base0 ^ (64 * dt))));
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_row0 + (base1 ^ (64 * dt))));

@@ -6,8 +6,9 @@
 // online softmax, tiling and fusion, one log-sum-exp per row). Only O and the
 // row log-sum-exp are written; the N x N scores stay in registers.
 //
-// Work decomposition: one 256-thread workgroup per (query tile of 128 rows,
-// batch, head); each of the 4 waves owns 32 query rows, and query tiles run
+// Work decomposition: one workgroup per (query tile, batch, head); each wave
+// owns 32 query rows (8 waves, 256 rows; 4 waves, 128 rows, for the
+// block-sparse mask, whose blocks are 128 rows), and query tiles run
 // in parallel over the sequence ("Core ideas": parallelism over the sequence
 // dimension). The workgroup streams 64-key tiles of K and V through LDS,
 // double-buffered: tile t+1 is copied global -> LDS asynchronously (no
@@ -35,10 +36,21 @@
 
 namespace fa {
 
-constexpr int kFwdBR = 128;      // queries per workgroup
 constexpr int kFwdBC = 64;       // keys per LDS tile
-constexpr int kFwdThreads = 256;
 constexpr int kMaskBlock = 128;  // block-sparse mask granularity
+
+// Waves per workgroup (32 query rows each). Eight waves share every K/V tile
+// copied into LDS among 256 queries; block-sparse keeps four so that a
+// workgroup's queries stay inside one 128-row mask block.
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 4
+#endif
+template <int D, int MASK>
+struct FwdShape {
+  static constexpr int NW = MASK == 2 ? 4 : FA_FWD_WAVES;
+  static constexpr int BR = 32 * NW;
+  static constexpr int THREADS = 64 * NW;
+};
 
 template <int D>
 struct alignas(16) FwdSmem {
@@ -49,8 +61,12 @@ struct alignas(16) FwdSmem {
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 template <int D, int MASK>
-__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3))) void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
+__global__ __launch_bounds__((FwdShape<D, MASK>::THREADS))
+__attribute__((amdgpu_waves_per_eu(D == 128 || FwdShape<D, MASK>::NW == 8 ? 2 : 3)))
+void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   __shared__ FwdSmem<D> sm;
+  constexpr int NW = FwdShape<D, MASK>::NW;
+  constexpr int kFwdBR = FwdShape<D, MASK>::BR;
   constexpr int TPB = kMaskBlock / kFwdBC;                 // key tiles per mask block
   constexpr int NDT = D / 32;                              // 32-row blocks of O^T
 
@@ -84,8 +100,8 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(D =
     return t < kend ? t : kend;
   };
   auto issue = [&](int kt, int buf) {
-    tile_load_async<D, kFwdBC, 4>(sm.k[buf], Kh, kt * kFwdBC, N, w, lane);
-    tile_load_async<D, kFwdBC, 4>(sm.v[buf], Vh, kt * kFwdBC, N, w, lane);
+    tile_load_async<D, kFwdBC, NW>(sm.k[buf], Kh, kt * kFwdBC, N, w, lane);
+    tile_load_async<D, kFwdBC, NW>(sm.v[buf], Vh, kt * kFwdBC, N, w, lane);
   };
   const int kbase_l = row_frag_base<D>(lane);
   const int vbase0_l = col_frag_base<D>(lane, 0), vbase1_l = col_frag_base<D>(lane, 1);
@@ -118,25 +134,27 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(D =
   auto tile = [&](int buf, int kt, auto nm) {
     constexpr bool NM = decltype(nm)::value;
     const int k0 = kt * kFwdBC;
-    const uint8_t* kt_ = sm.k[buf];
-    const uint8_t* vt_ = sm.v[buf];
-    const bool live1 = !(MASK == 1 && k0 + 32 > qw0 + 31);
-    // Opaque copies of the per-lane bases: the compiler recomputes the few
-    // XORed fragment addresses here instead of keeping all of them live
-    // across the loop (which would cost 16 VGPRs).
-    int kbase = kbase_l, vbase0 = vbase0_l, vbase1 = vbase1_l;
+    // Lane addresses of this tile's fragments relative to the start of the
+    // shared block: the buffer offset (a multiple of 8 KiB) has no bits in
+    // the XORed chunk field, so base + offset can be XORed directly. The
+    // opaque copies make the compiler recompute the XORed addresses here
+    // rather than keep all of them live across the loop.
+    const uint8_t* sbase = (const uint8_t*)&sm;
+    int kbase = kbase_l + (int)(sm.k[buf] - sbase);
+    int vbase0 = vbase0_l + (int)(sm.v[buf] - sbase), vbase1 = vbase1_l + (int)(sm.v[buf] - sbase);
     asm volatile("" : "+v"(kbase), "+v"(vbase0), "+v"(vbase1));
+    const bool live1 = !(MASK == 1 && k0 + 32 > qw0 + 31);
 
     u32x4 kf[D / 16];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) kf[ks] = row_frag(kt_, kbase, ks);
+    for (int ks = 0; ks < D / 16; ++ks) kf[ks] = row_frag(sbase, kbase, ks);
     f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) s0 = mfma_32x32x16(kf[ks], qf[ks], s0);
     __builtin_amdgcn_sched_barrier(0);
     if (live1) {
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) kf[ks] = row_frag(kt_ + 32 * 2 * D, kbase, ks);
+      for (int ks = 0; ks < D / 16; ++ks) kf[ks] = row_frag(sbase + 32 * 2 * D, kbase, ks);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) s1 = mfma_32x32x16(kf[ks], qf[ks], s1);
     }
@@ -195,7 +213,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(D =
       for (int dt = 0; dt < NDT; ++dt) {
         u32x4 vf[2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) vf[st] = col_frag(vt_ + (kb * 32 + st * 16) * 2 * D, vbase0, vbase1, dt);
+        for (int st = 0; st < 2; ++st) vf[st] = col_frag(sbase + (kb * 32 + st * 16) * 2 * D, vbase0, vbase1, dt);
 #pragma unroll
         for (int st = 0; st < 2; ++st) acc[dt] = mfma_32x32x16(vf[st], pb[st], acc[dt]);
       }
@@ -255,11 +273,12 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(D =
 
 template <int D, int MASK>
 static int launch_fwd_t(const AttnParams& p, hipStream_t stream) {
-  const uint32_t nqt = (uint32_t)((p.N + kFwdBR - 1) / kFwdBR);
+  using S = FwdShape<D, MASK>;
+  const uint32_t nqt = (uint32_t)((p.N + S::BR - 1) / S::BR);
   const uint32_t total = nqt * (uint32_t)p.B * (uint32_t)p.H;
   AttnParams pp = p;
   void* args[] = {&pp, (void*)&nqt, (void*)&total};
-  return (int)hipLaunchKernel((const void*)&fwd_bf16_kernel<D, MASK>, dim3(total), dim3(kFwdThreads),
+  return (int)hipLaunchKernel((const void*)&fwd_bf16_kernel<D, MASK>, dim3(total), dim3(S::THREADS),
                               args, 0, stream);
 }
 
