@@ -32,6 +32,8 @@
 // lane, which lets P and dS feed the next product as B operands directly.
 // Both loop kernels double-buffer their LDS tiles: tile t+1 is copied while
 // tile t is computed.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -153,7 +155,14 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   const int rbase_l = row_frag_base<D>(lane);
   const int cbase0_l = col_frag_base<D>(lane, 0), cbase1_l = col_frag_base<D>(lane, 1);
 
-  auto compute = [&](int buf, int it) {
+  // One 64-query tile in stages over its two 32-query sub-blocks, ordered
+  // so the MFMA pipe and the VALU have independent work side by side:
+  //   S0, dP0 | S1, dP1 with P0, dS0 | dV, dK of block 0 with P1, dS1 |
+  //   dV, dK of block 1.
+  // NM selects the masked variant (diagonal and tail tiles only); in the
+  // unmasked one both sub-blocks are live and the stages are straight-line.
+  auto tile = [&](int buf, int it, auto nm) {
+    constexpr bool NM = decltype(nm)::value;
     const int q0 = it * kDkvBQ;
     // Per-tile lane addresses relative to the shared block (see the
     // forward kernel): one XOR per fragment, opaque so they are not all
@@ -163,19 +172,22 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     int qr = rbase_l + oq, orow = rbase_l + oo;
     int qc0 = cbase0_l + oq, qc1 = cbase1_l + oq, oc0 = cbase0_l + oo, oc1 = cbase1_l + oo;
     asm volatile("" : "+v"(qr), "+v"(orow), "+v"(qc0), "+v"(qc1), "+v"(oc0), "+v"(oc1));
+    bool live[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int qb0 = q0 + 32 * mb;
-      if (MASK == 1 && qb0 + 31 < kw0) continue;           // every query before this wave's keys
-      const bool needm = (MASK == 1 && qb0 < kw0 + 31) || qb0 + 32 > N;
-      f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        s = mfma_32x32x16(row_frag(sbase + mb * 32 * 2 * D, qr, ks), kf[ks], s);
+    for (int mb = 0; mb < 2; ++mb) live[mb] = !NM || !(MASK == 1 && q0 + 32 * mb + 31 < kw0);
+
+    auto sdp = [&](int mb, f32x16& sv, f32x16& dpv) {
+      sv = zero16();
+      dpv = zero16();
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        dp = mfma_32x32x16(row_frag(sbase + mb * 32 * 2 * D, orow, ks), vf[ks], dp);
-      u32x4 pb[2], db[2];
+        sv = mfma_32x32x16(row_frag(sbase + mb * 32 * 2 * D, qr, ks), kf[ks], sv);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        dpv = mfma_32x32x16(row_frag(sbase + mb * 32 * 2 * D, orow, ks), vf[ks], dpv);
+    };
+    // P = 2^(c s - LSE log2 e) and dS = P (dP - D), packed as B operands.
+    auto pds = [&](int mb, const f32x16& sv, const f32x16& dpv, u32x4 pb[2], u32x4 db[2]) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         float pv[8], dv[8];
@@ -190,13 +202,13 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * g + e;
-            float pp = fast_exp2(__builtin_fmaf(s[i], c, -lv[e] * kLog2e));
-            if (needm) {
+            float pp = fast_exp2(__builtin_fmaf(sv[i], c, -lv[e] * kLog2e));
+            if (NM) {
               const int q = q0 + ql + e;
               if (q >= N || (MASK == 1 && kj > q)) pp = 0.f;
             }
             pv[4 * g2 + e] = pp;
-            dv[4 * g2 + e] = pp * (dp[i] - dd[e]);
+            dv[4 * g2 + e] = pp * (dpv[i] - dd[e]);
           }
         }
         pb[st] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
@@ -204,6 +216,8 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
         db[st] = u32x4{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]),
                        pack_bf16x2(dv[4], dv[5]), pack_bf16x2(dv[6], dv[7])};
       }
+    };
+    auto dkdv = [&](int mb, const u32x4 pb[2], const u32x4 db[2]) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -212,7 +226,37 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
           dvT[dt] = mfma_32x32x16(col_frag(rowp, oc0, oc1, dt), pb[st], dvT[dt]);
           dkT[dt] = mfma_32x32x16(col_frag(rowp, qc0, qc1, dt), db[st], dkT[dt]);
         }
+    };
+
+    f32x16 s0, dp0, s1, dp1;
+    u32x4 pb0[2], db0[2], pb1[2], db1[2];
+    if (!NM) {
+      sdp(0, s0, dp0);
+      __builtin_amdgcn_sched_barrier(0);
+      sdp(1, s1, dp1);
+      pds(0, s0, dp0, pb0, db0);
+      __builtin_amdgcn_sched_barrier(0);
+      dkdv(0, pb0, db0);
+      pds(1, s1, dp1, pb1, db1);
+      __builtin_amdgcn_sched_barrier(0);
+      dkdv(1, pb1, db1);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        if (!live[mb]) continue;
+        sdp(mb, s0, dp0);
+        pds(mb, s0, dp0, pb0, db0);
+        dkdv(mb, pb0, db0);
+      }
     }
+  };
+  auto compute = [&](int buf, int it) {
+    const int q0 = it * kDkvBQ;
+    const bool needm = (MASK == 1 && q0 < kw0 + 31) || q0 + kDkvBQ > N;
+    if (needm)
+      tile(buf, it, std::true_type{});
+    else
+      tile(buf, it, std::false_type{});
   };
 
   wait_vmem();
