@@ -372,47 +372,86 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   const int rbase_l = row_frag_base<D>(lane);
   const int cbase0_l = col_frag_base<D>(lane, 0), cbase1_l = col_frag_base<D>(lane, 1);
 
-  auto compute = [&](int buf, int kt) {
+  // One 64-key tile in stages over its two 32-key sub-blocks (as in the
+  // dK/dV kernel): S0, dP0 | S1, dP1 with dS0 | dQ += K^T dS of block 0
+  // with dS1 | of block 1. NM selects the masked variant.
+  auto tile = [&](int buf, int kt, auto nm) {
+    constexpr bool NM = decltype(nm)::value;
     const int k0 = kt * kDqBK;
-    if (MASK == 1 && k0 > qw0 + 31) return;
     const uint8_t* sbase = (const uint8_t*)&sm;
     const int ok = (int)(sm.k[buf] - sbase), ov = (int)(sm.v[buf] - sbase);
     int kr = rbase_l + ok, vr = rbase_l + ov, kc0 = cbase0_l + ok, kc1 = cbase1_l + ok;
     asm volatile("" : "+v"(kr), "+v"(vr), "+v"(kc0), "+v"(kc1));
-    const bool need_mask = (k0 + kDqBK > N) || (MASK == 1 && k0 + kDqBK - 1 > qw0);
+    bool live[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (MASK == 1 && k0 + kb * 32 > qw0 + 31) continue;
-      f32x16 s = zero16(), dp = zero16();
+    for (int kb = 0; kb < 2; ++kb) live[kb] = !NM || !(MASK == 1 && k0 + kb * 32 > qw0 + 31);
+
+    auto sdp = [&](int kb, f32x16& sv, f32x16& dpv) {
+      sv = zero16();
+      dpv = zero16();
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        s = mfma_32x32x16(row_frag(sbase + kb * 32 * 2 * D, kr, ks), qf[ks], s);
+        sv = mfma_32x32x16(row_frag(sbase + kb * 32 * 2 * D, kr, ks), qf[ks], sv);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        dp = mfma_32x32x16(row_frag(sbase + kb * 32 * 2 * D, vr, ks), of[ks], dp);
-      u32x4 db[2];
+        dpv = mfma_32x32x16(row_frag(sbase + kb * 32 * 2 * D, vr, ks), of[ks], dpv);
+    };
+    auto ds = [&](int kb, const f32x16& sv, const f32x16& dpv, u32x4 db[2]) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         float y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * st + e;
-          float pp = fast_exp2(__builtin_fmaf(s[i], c, -lse2));
-          if (need_mask) {
+          float pp = fast_exp2(__builtin_fmaf(sv[i], c, -lse2));
+          if (NM) {
             const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
             if (key >= N || (MASK == 1 && key > qi)) pp = 0.f;
           }
-          y[e] = pp * (dp[i] - dti);
+          y[e] = pp * (dpv[i] - dti);
         }
         db[st] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
                        pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
       }
+    };
+    auto dqacc = [&](int kb, const u32x4 db[2]) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
           dqT[dt] = mfma_32x32x16(col_frag(sbase + (kb * 32 + st * 16) * 2 * D, kc0, kc1, dt), db[st], dqT[dt]);
+    };
+
+    f32x16 s0, dp0, s1, dp1;
+    u32x4 db0[2], db1[2];
+    if (!NM) {
+      sdp(0, s0, dp0);
+      __builtin_amdgcn_sched_barrier(0);
+      sdp(1, s1, dp1);
+      ds(0, s0, dp0, db0);
+      __builtin_amdgcn_sched_barrier(0);
+      dqacc(0, db0);
+      ds(1, s1, dp1, db1);
+      __builtin_amdgcn_sched_barrier(0);
+      dqacc(1, db1);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (!live[kb]) continue;
+        sdp(kb, s0, dp0);
+        ds(kb, s0, dp0, db0);
+        dqacc(kb, db0);
+      }
     }
+  };
+  auto compute = [&](int buf, int kt) {
+    const int k0 = kt * kDqBK;
+    if (MASK == 1 && k0 > qw0 + 31) return;
+    const bool need_mask = (k0 + kDqBK > N) || (MASK == 1 && k0 + kDqBK - 1 > qw0);
+    if (need_mask)
+      tile(buf, kt, std::true_type{});
+    else
+      tile(buf, kt, std::false_type{});
   };
 
   wait_vmem();
