@@ -143,16 +143,20 @@ def summarize_trace(db_path: str) -> str:
 
 
 def _pmc_means(db_path: str, counter: str) -> dict:
+    """Mean counter value per dispatch of each kernel. For the copy kernel the
+    largest dispatch is taken: the calibration copy is the biggest one (input
+    uploads can run small copies through the same kernel)."""
     import collections
     import sqlite3
     cur = sqlite3.connect(db_path).cursor()
-    acc = collections.defaultdict(float)
-    disp = collections.defaultdict(set)
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
     for name, did, val in cur.execute(
             "select kernel_name, dispatch_id, value from counters_collection where counter_name = ?", (counter,)):
-        acc[name] += val
-        disp[name].add(did)
-    return {n: acc[n] / len(disp[n]) for n in acc}
+        per[name][did] += val
+    out = {}
+    for n, d in per.items():
+        out[n] = max(d.values()) if COPY_KERNEL in n else sum(d.values()) / len(d)
+    return out
 
 
 def summarize_traffic(fetch_db: str, write_db: str, workload: str, copy_bytes: int, update: bool) -> str:
