@@ -303,8 +303,9 @@ struct alignas(16) DqSmem {
   uint8_t v[2][kDqBK * D * 2];   // swizzled row-major V tiles
 };
 
+// d = 64 fits three waves per SIMD (<= 168 VGPRs, 32 KiB LDS per workgroup).
 template <int D, int MASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3)))
 void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   __shared__ DqSmem<D> sm;
   constexpr int NDT = D / 32;

@@ -147,6 +147,24 @@ __device__ __forceinline__ u32x4 col_frag(const uint8_t* tile_row0, int base0, i
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
+// A chain of NOPS MFMAs whose A fragments come from LDS, with the fragment
+// reads issued LA operations ahead of their use so LDS latency overlaps the
+// preceding MFMAs: load(i) returns fragment i, op(i, frag) issues MFMA i.
+template <int NOPS, int LA, class LoadF, class OpF>
+__device__ __forceinline__ void lds_pipelined(LoadF&& load, OpF&& op) {
+  static_assert(LA >= 1, "lookahead");
+  constexpr int L = LA < NOPS ? LA : NOPS;
+  u32x4 fr[L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) fr[j] = load(j);
+#pragma unroll
+  for (int i = 0; i < NOPS; ++i) {
+    const u32x4 cur = fr[i % L];
+    if (i + L < NOPS) fr[i % L] = load(i + L);
+    op(i, cur);
+  }
+}
+
 // Workgroup id -> logical tile id so that consecutive logical tiles (the query
 // tiles of one head) run on the same XCD and share its L2. Hardware hands out
 // workgroup ids round-robin over the 8 XCDs; this maps XCD x to the contiguous
