@@ -118,10 +118,12 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     const int t = nb == blk ? it : nb * QPB;
     return t < nqt ? t : nqt;
   };
+  TileLoader<D, kDkvBQ, 4> ld;
+  ld.init(w, lane);
   auto issue = [&](int it, int buf) {
     const int q0 = it * kDkvBQ;
-    tile_load_async<D, kDkvBQ, 4>(sm.q[buf], Qh, q0, N, w, lane);
-    tile_load_async<D, kDkvBQ, 4>(sm.dO[buf], dOh, q0, N, w, lane);
+    ld.load(sm.q[buf], Qh, q0, N);
+    ld.load(sm.dO[buf], dOh, q0, N);
     if (w < 2) {   // one dword per lane: 64 row statistics per tile
       const int q = min(q0 + lane, N - 1);
       const float* src = w == 0 ? lseh + q : dth + q;
@@ -303,9 +305,12 @@ struct alignas(16) DqSmem {
   uint8_t v[2][kDqBK * D * 2];   // swizzled row-major V tiles
 };
 
-// d = 64 fits three waves per SIMD (<= 168 VGPRs, 32 KiB LDS per workgroup).
+// d = 64 fits three waves per SIMD (<= 168 VGPRs, 32 KiB LDS per workgroup);
+// d = 128 two, except with the block-sparse mask scanner, which needs the
+// registers of one wave per SIMD to stay free of spills.
 template <int D, int MASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? (MASK == 2 ? 1 : 2) : 3)))
 void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   __shared__ DqSmem<D> sm;
   constexpr int NDT = D / 32;
@@ -340,9 +345,11 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     const int t = nb == blk ? kt : nb * TPB;
     return t < kend ? t : kend;
   };
+  TileLoader<D, kDqBK, 4> ld;
+  ld.init(w, lane);
   auto issue = [&](int kt, int buf) {
-    tile_load_async<D, kDqBK, 4>(sm.k[buf], Kh, kt * kDqBK, N, w, lane);
-    tile_load_async<D, kDqBK, 4>(sm.v[buf], Vh, kt * kDqBK, N, w, lane);
+    ld.load_recompute(sm.k[buf], Kh, kt * kDqBK, N);
+    ld.load(sm.v[buf], Vh, kt * kDqBK, N);
   };
 
   int kt = next_tile(0);

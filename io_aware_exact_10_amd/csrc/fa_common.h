@@ -90,26 +90,61 @@ __device__ __forceinline__ int tile_off(int r, int col) {
 // swizzled LDS tile, straight from global memory to LDS (no registers).
 // Each wave instruction fills one contiguous KiB: lane i writes bytes
 // [16 i, 16 i + 16), so lane i fetches the global chunk that belongs there.
-// Rows past N read row N - 1 (finite data the callers mask or ignore).
+// The byte offset of that chunk from the tile's first row does not depend on
+// the tile, so it is computed once per lane (offs); a full tile is then one
+// uniform base pointer plus offs[i] per instruction. Rows past N (only in
+// the last tile) read row N - 1: finite data the callers mask or ignore.
 // Completion: s_waitcnt vmcnt(0) then a workgroup barrier.
 template <int D, int ROWS, int NWAVES>
-__device__ __forceinline__ void tile_load_async(uint8_t* tile, const uint16_t* __restrict__ X, int r0, int N,
-                                                int wave, int lane) {
-  constexpr int RPK = 1024 / (2 * D);   // rows per KiB
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int NK = ROWS / RPK;        // KiB pieces per tile
+struct TileLoader {
+  static constexpr int RPK = 1024 / (2 * D);   // rows per KiB
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int NK = ROWS / RPK;        // KiB pieces per tile
+  static constexpr int PER = NK / NWAVES;      // pieces per wave
   static_assert(NK % NWAVES == 0, "tile pieces per wave");
-#pragma unroll
-  for (int i = 0; i < NK / NWAVES; ++i) {
-    const int ci = wave + i * NWAVES;
+  int offs[PER];                               // bytes from the tile's first row
+  int wave, lane_;
+
+  __device__ __forceinline__ static int offset(int w, int lane, int i) {
+    const int ci = w + i * NWAVES;
     const int row = ci * RPK + lane / CPR;
-    const int c = (lane % CPR) ^ swz<D>(row);
-    int gr = r0 + row;
-    gr = gr < N ? gr : N - 1;
-    __builtin_amdgcn_global_load_lds((const void*)(X + (size_t)gr * D + c * 8), (lds_void*)(tile + ci * 1024),
-                                     16, 0, 0);
+    return row * (2 * D) + (((lane % CPR) ^ swz<D>(row)) << 4);
   }
-}
+  __device__ __forceinline__ void init(int w, int lane) {
+    wave = w;
+    lane_ = lane;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) offs[i] = offset(w, lane, i);
+  }
+  // Same as load() with the offsets recomputed at the call (no registers kept
+  // live across the loop), for kernels short of VGPRs.
+  __device__ __forceinline__ void load_recompute(uint8_t* tile, const uint16_t* __restrict__ X, int r0, int N) {
+    int l = lane_;
+    asm volatile("" : "+v"(l));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) offs[i] = offset(wave, l, i);
+    load(tile, X, r0, N);
+  }
+  __device__ __forceinline__ void load(uint8_t* tile, const uint16_t* __restrict__ X, int r0, int N) const {
+    const uint8_t* base = (const uint8_t*)(X + (size_t)r0 * D);
+    if (r0 + ROWS <= N) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(base + offs[i]), (lds_void*)(tile + (wave + i * NWAVES) * 1024),
+                                         16, 0, 0);
+    } else {
+      const int last = (N - 1 - r0) * (2 * D);   // first byte of row N - 1, relative to row r0
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        int o = offs[i];
+        const int row_off = o & ~(2 * D - 1);
+        if (row_off > last) o = last + (o & (2 * D - 1));
+        __builtin_amdgcn_global_load_lds((const void*)(base + o), (lds_void*)(tile + (wave + i * NWAVES) * 1024),
+                                         16, 0, 0);
+      }
+    }
+  }
+};
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

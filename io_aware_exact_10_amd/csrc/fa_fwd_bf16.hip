@@ -99,9 +99,11 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     const int t = nb == blk ? kt : nb * TPB;
     return t < kend ? t : kend;
   };
+  TileLoader<D, kFwdBC, NW> ld;
+  ld.init(w, lane);
   auto issue = [&](int kt, int buf) {
-    tile_load_async<D, kFwdBC, NW>(sm.k[buf], Kh, kt * kFwdBC, N, w, lane);
-    tile_load_async<D, kFwdBC, NW>(sm.v[buf], Vh, kt * kFwdBC, N, w, lane);
+    ld.load(sm.k[buf], Kh, kt * kFwdBC, N);
+    ld.load(sm.v[buf], Vh, kt * kFwdBC, N);
   };
   const int kbase_l = row_frag_base<D>(lane);
   const int vbase0_l = col_frag_base<D>(lane, 0), vbase1_l = col_frag_base<D>(lane, 1);
