@@ -12,8 +12,11 @@ from .attention import (  # noqa: F401
     MASK_NONE,
     backward,
     backward_head,
+    backward_varlen,
+    causal_offset,
     forward,
     forward_head,
+    forward_varlen,
     online_forward_head,
     online_softmax_row,
     probabilities_head,

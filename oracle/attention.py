@@ -32,9 +32,20 @@ statistics). The oracle's backward is the derivative of the definition above:
     dQ = scale * dS K;  dK = scale * dS^T Q
 
 Visibility: mask_kind 0 = every key; 1 = causal (key j visible to query i iff
-j <= i, query and key sequences of equal length); 2 = block-sparse ([R] "The
-method", block-sparse extension): key j visible to query i iff
+j <= i + offset, where offset = Nk - Nq aligns the last query with the last
+key and is 0 for equal lengths); 2 = block-sparse ([R] "The method",
+block-sparse extension): key j visible to query i iff
 block_mask[i // block, j // block] != 0, one mask shared by all heads.
+
+Packed variable-length batches and shared K/V heads ([T] "Flash Attention 2
+(2023)": variable sequence lengths and multi-/grouped-query attention; [P]
+"Implementation: Is It Hard to Adopt?": ragged batches without padding):
+sequence b owns query tokens [cu_q[b], cu_q[b+1]) and key tokens
+[cu_k[b], cu_k[b+1]) of tensors laid out [tokens, heads, d]; each sequence
+is an independent attention problem, and query head h reads K/V head
+h // (H // Hkv). The pages give no alignment rule for causal attention with
+unequal lengths; the offset above (queries are the last Nq positions of the
+key sequence) is the reading taken.
 
 A query row with no visible key has O = 0, LSE = -inf and contributes no
 gradient (it cannot occur for causal or unmasked attention).
@@ -57,18 +68,20 @@ MASK_BLOCK_SPARSE = 2
 # ----------------------------------------------------------------------------
 # visibility
 # ----------------------------------------------------------------------------
-def visible(rows: np.ndarray, N: int, mask_kind: int, block_mask=None, block: int = 128) -> np.ndarray:
+def visible(rows: np.ndarray, N: int, mask_kind: int, block_mask=None, block: int = 128,
+            offset: int = 0) -> np.ndarray:
     """Boolean [len(rows), N]: True where key j is visible to query rows[r].
 
-    Causal: [C] "How to approach it" (check with and without a causal mask);
-    block-sparse: [R] "The method" (block-sparse extension).
+    Causal: [C] "How to approach it" (check with and without a causal mask),
+    key j visible to query i iff j <= i + offset; block-sparse: [R] "The
+    method" (block-sparse extension).
     """
     rows = np.asarray(rows)
     cols = np.arange(N)
     if mask_kind == MASK_NONE:
         return np.ones((rows.size, N), dtype=bool)
     if mask_kind == MASK_CAUSAL:
-        return cols[None, :] <= rows[:, None]
+        return cols[None, :] <= rows[:, None] + offset
     if mask_kind == MASK_BLOCK_SPARSE:
         bm = np.asarray(block_mask) != 0
         return bm[(rows // block)[:, None], (cols // block)[None, :]]
@@ -82,30 +95,38 @@ def _f64(x):
 # ----------------------------------------------------------------------------
 # the definition (one head)
 # ----------------------------------------------------------------------------
-def _scores(qc, k, scale, rows, N, mask_kind, block_mask, block):
+def causal_offset(nq: int, nk: int) -> int:
+    """Causal offset for Nq queries against Nk keys: the last query sees
+    every key (Nk - Nq; 0 for equal lengths)."""
+    return nk - nq
+
+
+def _scores(qc, k, scale, rows, N, mask_kind, block_mask, block, offset=0):
     s = scale * (qc @ k.T)
-    vis = visible(rows, N, mask_kind, block_mask, block)
+    vis = visible(rows, N, mask_kind, block_mask, block, offset)
     s[~vis] = -np.inf
     return s, vis
 
 
 def forward_head(q, k, v, scale, mask_kind=MASK_NONE, block_mask=None, rows=None,
-                 block: int = 128, chunk: int = 2048):
+                 block: int = 128, chunk: int = 2048, offset=None):
     """O [n, d] and LSE [n] (natural log) of one head for query ``rows``.
 
     Safe softmax with the row max subtracted ([T] "Online Softmax Algorithm",
     safe softmax) applied to masked, scaled scores; O = P V ([T] "The Memory
     Wall Problem"). ``rows`` defaults to every query; S is materialised for
-    ``chunk`` rows at a time.
+    ``chunk`` rows at a time. q is [Nq, d], k and v [Nk, d]; the causal
+    offset defaults to ``causal_offset(Nq, Nk)``.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     N = k.shape[0]
+    offset = causal_offset(q.shape[0], N) if offset is None else offset
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     o = np.zeros((rows.size, v.shape[1]))
     lse = np.full(rows.size, -np.inf)
     for c0 in range(0, rows.size, chunk):
         r = rows[c0:c0 + chunk]
-        s, vis = _scores(q[r], k, scale, r, N, mask_kind, block_mask, block)
+        s, vis = _scores(q[r], k, scale, r, N, mask_kind, block_mask, block, offset)
         live = vis.any(axis=1)
         m = np.where(live, s.max(axis=1), 0.0)
         e = np.exp(s - m[:, None])                 # exp(-inf) = 0 on masked keys
@@ -117,12 +138,14 @@ def forward_head(q, k, v, scale, mask_kind=MASK_NONE, block_mask=None, rows=None
     return o, lse
 
 
-def probabilities_head(q, k, scale, mask_kind=MASK_NONE, block_mask=None, rows=None, block=128):
-    """P [n, N] of one head (small inputs only; used by the invariant pins)."""
+def probabilities_head(q, k, scale, mask_kind=MASK_NONE, block_mask=None, rows=None, block=128,
+                       offset=None):
+    """P [n, Nk] of one head (small inputs only; used by the invariant pins)."""
     q, k = _f64(q), _f64(k)
     N = k.shape[0]
+    offset = causal_offset(q.shape[0], N) if offset is None else offset
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
-    s, vis = _scores(q[rows], k, scale, rows, N, mask_kind, block_mask, block)
+    s, vis = _scores(q[rows], k, scale, rows, N, mask_kind, block_mask, block, offset)
     live = vis.any(axis=1)
     m = np.where(live, s.max(axis=1), 0.0)
     e = np.exp(s - m[:, None])
@@ -131,7 +154,7 @@ def probabilities_head(q, k, scale, mask_kind=MASK_NONE, block_mask=None, rows=N
 
 
 def backward_head(q, k, v, do, scale, mask_kind=MASK_NONE, block_mask=None,
-                  block: int = 128, chunk: int = 2048):
+                  block: int = 128, chunk: int = 2048, offset=None):
     """dQ, dK, dV of one head: the analytic derivative of ``forward_head``.
 
     P is rebuilt from Q, K and the row log-sum-exp, the same statistics the
@@ -140,13 +163,14 @@ def backward_head(q, k, v, do, scale, mask_kind=MASK_NONE, block_mask=None,
     calculus on the definition; no page prints them.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    N = q.shape[0]
+    Nq, Nk = q.shape[0], k.shape[0]
+    offset = causal_offset(Nq, Nk) if offset is None else offset
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for c0 in range(0, N, chunk):
-        r = np.arange(c0, min(N, c0 + chunk))
-        s, vis = _scores(q[r], k, scale, r, N, mask_kind, block_mask, block)
+    for c0 in range(0, Nq, chunk):
+        r = np.arange(c0, min(Nq, c0 + chunk))
+        s, vis = _scores(q[r], k, scale, r, Nk, mask_kind, block_mask, block, offset)
         live = vis.any(axis=1)
         m = np.where(live, s.max(axis=1), 0.0)
         e = np.exp(s - m[:, None])
@@ -191,6 +215,60 @@ def backward(q, k, v, do, scale, mask_kind=MASK_NONE, block_mask=None, heads=Non
     out = [backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, mask_kind, block_mask, block)
            for b, h in heads]
     return tuple(np.stack([g[i] for g in out]) for i in range(3))
+
+
+# ----------------------------------------------------------------------------
+# packed variable-length batches with shared K/V heads
+# ----------------------------------------------------------------------------
+def _spans(cu):
+    cu = [int(x) for x in np.asarray(cu)]
+    return [(cu[b], cu[b + 1]) for b in range(len(cu) - 1)]
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, scale, mask_kind=MASK_NONE):
+    """Packed batch forward: q [Tq, H, d], k and v [Tk, Hkv, d].
+
+    Sequence b is the ordinary attention problem on its own tokens; query
+    head h reads K/V head h // (H // Hkv). Returns O [Tq, H, d] and LSE
+    [H, Tq]; tokens outside every sequence keep O = 0 and LSE = -inf.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Tq, H, d = q.shape
+    G = H // k.shape[1]
+    o = np.zeros((Tq, H, v.shape[2]))
+    lse = np.full((H, Tq), -np.inf)
+    for (q0, q1), (k0, k1) in zip(_spans(cu_q), _spans(cu_k)):
+        if q1 == q0:
+            continue
+        for h in range(H):
+            ob, lb = forward_head(q[q0:q1, h], k[k0:k1, h // G], v[k0:k1, h // G], scale, mask_kind)
+            o[q0:q1, h] = ob
+            lse[h, q0:q1] = lb
+    return o, lse
+
+
+def backward_varlen(q, k, v, do, cu_q, cu_k, scale, mask_kind=MASK_NONE):
+    """Packed batch backward: dQ [Tq, H, d], dK and dV [Tk, Hkv, d].
+
+    A K/V head's gradients sum the contributions of every query head that
+    reads it (the chain rule through the shared operand).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    H = q.shape[1]
+    G = H // k.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for (q0, q1), (k0, k1) in zip(_spans(cu_q), _spans(cu_k)):
+        if q1 == q0 or k1 == k0:
+            continue
+        for h in range(H):
+            a, b, c = backward_head(q[q0:q1, h], k[k0:k1, h // G], v[k0:k1, h // G], do[q0:q1, h],
+                                    scale, mask_kind)
+            dq[q0:q1, h] = a
+            dk[k0:k1, h // G] += b
+            dv[k0:k1, h // G] += c
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------------------

@@ -346,3 +346,97 @@ def test_attention_matrix_memory_table():
     P = oracle.probabilities_head(np.zeros((2048, 1)), np.zeros((2048, 1)), 1.0)
     assert P.size == parse(tab["rows"][0]["elements"])
     assert P.astype(np.float32).nbytes == parse(tab["rows"][0]["fp32"])
+
+
+# --------------------------------------------------------------------------
+# unequal lengths, shared K/V heads and packed batches ([T] "Flash Attention 2
+# (2023)"; [P] "Implementation: Is It Hard to Adopt?"), pinned against torch's
+# float64 SDPA + autograd with masks built here, independently of the oracle
+# --------------------------------------------------------------------------
+def _sdpa_grads(q, k, v, do, scale, vis):
+    """q [H, Nq, d], k, v [Hkv, Nk, d] (repeated per group inside torch, so
+    autograd sums the group's contributions); vis [Nq, Nk] bool."""
+    H, Hkv = q.shape[0], k.shape[0]
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    kk = tk.repeat_interleave(H // Hkv, dim=0)
+    vv = tv.repeat_interleave(H // Hkv, dim=0)
+    m = torch.tensor(vis)
+    out = torch.nn.functional.scaled_dot_product_attention(tq[None], kk[None], vv[None],
+                                                           attn_mask=m[None, None], scale=scale)[0]
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    s = (scale * (tq @ kk.transpose(1, 2))).masked_fill(~m, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return [x.detach().numpy() for x in (out, lse, tq.grad, tk.grad, tv.grad)]
+
+
+@pytest.mark.parametrize("nq,nk", [(5, 23), (17, 17), (1, 40), (31, 64)])
+def test_causal_offset_matches_bottom_right_sdpa(nq, nk):
+    """Nq <= Nk: query i sees keys 0 .. i + Nk - Nq (the last query sees all)."""
+    d, sc = 6, 0.45
+    q, k, v, do = rnd(201, 1, nq, d), rnd(202, 1, nk, d), rnd(203, 1, nk, d), rnd(204, 1, nq, d)
+    vis = np.tril(np.ones((nq, nk), bool), k=nk - nq)
+    assert vis[-1].all() and vis[0].sum() == nk - nq + 1
+    ro, rl, rdq, rdk, rdv = _sdpa_grads(q, k, v, do, sc, vis)
+    O, L = oracle.forward_head(q[0], k[0], v[0], sc, MASK_CAUSAL, chunk=4)
+    dq, dk, dv = oracle.backward_head(q[0], k[0], v[0], do[0], sc, MASK_CAUSAL, chunk=3)
+    for a, b in ((O, ro[0]), (L, rl[0]), (dq, rdq[0]), (dk, rdk[0]), (dv, rdv[0])):
+        assert np.abs(a - b).max() <= 1e-12 * max(1.0, np.abs(b).max())
+    # the same numbers as the last Nq rows of the square causal problem
+    qf = np.vstack([rnd(205, nk - nq, d), q[0]])
+    Of, Lf = oracle.forward_head(qf, k[0], v[0], sc, MASK_CAUSAL)
+    assert np.allclose(O, Of[nk - nq:], rtol=0, atol=1e-13)
+    assert np.allclose(L, Lf[nk - nq:], rtol=0, atol=1e-13)
+
+
+def test_causal_offset_more_queries_than_keys():
+    """Nq > Nk: the first Nq - Nk queries see no key (O = 0, LSE = -inf, no
+    gradient); the rest match the bottom-right SDPA."""
+    nq, nk, d, sc = 20, 12, 5, 0.7
+    q, k, v, do = rnd(211, nq, d), rnd(212, nk, d), rnd(213, nk, d), rnd(214, nq, d)
+    O, L = oracle.forward_head(q, k, v, sc, MASK_CAUSAL)
+    dq, dk, dv = oracle.backward_head(q, k, v, do, sc, MASK_CAUSAL)
+    e = nq - nk
+    assert (O[:e] == 0).all() and np.isneginf(L[:e]).all() and (dq[:e] == 0).all()
+    vis = np.tril(np.ones((nk, nk), bool))
+    ro, rl, rdq, rdk, rdv = _sdpa_grads(q[None, e:], k[None], v[None], do[None, e:], sc, vis)
+    for a, b in ((O[e:], ro[0]), (L[e:], rl[0]), (dq[e:], rdq[0]), (dk, rdk[0]), (dv, rdv[0])):
+        assert np.abs(a - b).max() <= 1e-12 * max(1.0, np.abs(b).max())
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 1), (3, 3)])
+@pytest.mark.parametrize("mask_kind", [MASK_NONE, MASK_CAUSAL])
+def test_varlen_gqa_matches_per_sequence_sdpa(H, Hkv, mask_kind):
+    """Packed [tokens, heads, d] batches with K/V heads shared by groups of
+    query heads: each sequence against torch SDPA on that sequence alone."""
+    d, sc = 8, 0.35
+    lq, lk = [7, 1, 19, 0, 12], [7, 9, 25, 4, 12]
+    if mask_kind == MASK_NONE:
+        lk = [7, 9, 3, 4, 12]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+    q, k, v, do = rnd(221, Tq, H, d), rnd(222, Tk, Hkv, d), rnd(223, Tk, Hkv, d), rnd(224, Tq, H, d)
+    O, L = oracle.forward_varlen(q, k, v, cu_q, cu_k, sc, mask_kind)
+    dq, dk, dv = oracle.backward_varlen(q, k, v, do, cu_q, cu_k, sc, mask_kind)
+    assert O.shape == (Tq, H, d) and L.shape == (H, Tq) and dk.shape == (Tk, Hkv, d)
+    for b in range(len(lq)):
+        qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        if lq[b] == 0:
+            assert (dk[ks] == 0).all() and (dv[ks] == 0).all()
+            continue
+        vis = np.ones((lq[b], lk[b]), bool)
+        if mask_kind == MASK_CAUSAL:
+            vis = np.tril(vis, k=lk[b] - lq[b])
+        t = lambda a, s: np.ascontiguousarray(a[s].transpose(1, 0, 2))
+        ro, rl, rdq, rdk, rdv = _sdpa_grads(t(q, qs), t(k, ks), t(v, ks), t(do, qs), sc, vis)
+        for a, r in ((t(O, qs), ro), (L[:, qs], rl), (t(dq, qs), rdq), (t(dk, ks), rdk), (t(dv, ks), rdv)):
+            assert np.abs(a - r).max() <= 1e-12 * max(1.0, np.abs(r).max()), b
+
+
+def test_varlen_single_sequence_equals_dense_heads():
+    """One packed sequence with Hkv = H is the dense per-head problem."""
+    N, H, d, sc = 21, 3, 4, 0.6
+    q, k, v = rnd(231, N, H, d), rnd(232, N, H, d), rnd(233, N, H, d)
+    O, L = oracle.forward_varlen(q, k, v, [0, N], [0, N], sc, MASK_CAUSAL)
+    for h in range(H):
+        Oh, Lh = oracle.forward_head(q[:, h], k[:, h], v[:, h], sc, MASK_CAUSAL)
+        assert np.array_equal(O[:, h], Oh) and np.array_equal(L[h], Lh)
