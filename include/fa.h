@@ -134,6 +134,70 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, con
               int mask_kind, const uint8_t* block_mask, int dtype,
               const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Packed variable-length batches, unequal query and key lengths, and K/V
+ * heads shared by groups of query heads (multi-query and grouped-query
+ * attention). Passages: "Flash Attention — Revolutionizing Transformer
+ * Efficiency Through Memory-Aware Algorithms", "Flash Attention 2 (2023)"
+ * (variable sequence lengths; multi-query and grouped-query attention);
+ * "Flash Attention: Speeding Up LLM Inference and Training", "Implementation:
+ * Is It Hard to Adopt?" (ragged batches without padding). Each sequence is
+ * the attention problem defined above on its own tokens.
+ *
+ * Layout. q, o, dO, dq: [total_q, H, d]; k, v, dk, dv: [total_k, Hkv, d]
+ *   (token-major, d fastest), bfloat16. lse and the backward's row term:
+ *   float [H, total_q].
+ * Sequences. cu_seqlens_q and cu_seqlens_k are DEVICE int32 arrays of B + 1
+ *   non-decreasing token offsets, the first >= 0, the last <= total_q
+ *   (total_k). Sequence b owns query tokens [cu_seqlens_q[b],
+ *   cu_seqlens_q[b+1]) (nq_b of them) and key tokens [cu_seqlens_k[b],
+ *   cu_seqlens_k[b+1]) (nk_b). max_seqlen_q >= every nq_b and
+ *   max_seqlen_k >= every nk_b: they size the launch, since the library does
+ *   not read the offsets on the host. Offsets outside this contract are
+ *   clamped on the device, so no access leaves the tensors, but that
+ *   sequence's results are unspecified.
+ * Heads. H query heads, Hkv key/value heads, H a multiple of Hkv; query
+ *   head h reads K/V head h / (H / Hkv) (Hkv = H: multi-head; Hkv = 1:
+ *   multi-query). dk and dv of a K/V head sum the contributions of its
+ *   H / Hkv query heads.
+ * Causal. Key j of a sequence is visible to its query i iff
+ *   j <= i + nk_b - nq_b: the last query sees every key; with nq_b > nk_b the
+ *   first nq_b - nk_b queries see none (O row 0, lse -inf, no gradient).
+ *   With nq_b = nk_b this is the causal mask of the dense calls.
+ * Supported. dtype FA_BF16 only (FA_F32 returns FA_ERR_UNSUPPORTED);
+ *   mask_kind FA_MASK_NONE or FA_MASK_CAUSAL (FA_MASK_BLOCK_SPARSE returns
+ *   FA_ERR_MASK); d in {64, 128}; 1 <= H <= 65536.
+ * Untouched rows. Query-token rows of o, lse and dq, and key-token rows of dk
+ *   and dv, that belong to no sequence are not written. Key tokens of a
+ *   sequence with no queries get dk = dv = 0.
+ * Errors, alignment (cu_seqlens 4-byte aligned), overlap rules and
+ *   asynchrony are those of the dense calls; FA_ERR_SHAPE also covers
+ *   B, H, Hkv, max_seqlen or total < 1 and H not a multiple of Hkv.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int B, int H, int Hkv, int max_seqlen_q, int max_seqlen_k,
+                  int total_q, int total_k, int d, float scale, int mask_kind,
+                  int dtype, hipStream_t stream);
+
+/* Workspace bytes fa_bwd_varlen needs (the float row term [H, total_q],
+ * rounded up to 256 bytes); 0 for an invalid shape. */
+size_t fa_bwd_varlen_workspace_bytes(int total_q, int H, int d);
+
+/*
+ * Backward of fa_fwd_varlen: reads q, k, v, o, lse (as fa_fwd_varlen wrote
+ * them) and dO; writes dq [total_q, H, d], dk and dv [total_k, Hkv, d]. The
+ * same three kernels as fa_bwd run in order on `stream`; workspace is
+ * caller-owned device memory of at least fa_bwd_varlen_workspace_bytes()
+ * bytes, 16-byte aligned, contents ignored on entry.
+ */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dO, void* dq, void* dk, void* dv,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int B, int H, int Hkv, int max_seqlen_q, int max_seqlen_k,
+                  int total_q, int total_k, int d, float scale, int mask_kind, int dtype,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a fa_status value ("unknown status" otherwise). */
 const char* fa_status_string(int status);
 

@@ -5,9 +5,12 @@ the HIP kernels behind the C ABI declared in ``include/fa.h``. PyTorch
 supplies device memory and the current stream; nothing here computes.
 
 Low-level calls mirror the C ABI names (``fa_fwd``, ``fa_bwd``,
-``fa_bwd_workspace_bytes``, ``fa_status_string``) and take raw integer
+``fa_bwd_workspace_bytes``, ``fa_status_string``, ``fa_fwd_varlen``,
+``fa_bwd_varlen``, ``fa_bwd_varlen_workspace_bytes``) and take raw integer
 device pointers. ``forward`` / ``backward`` are conveniences that take torch
-tensors of shape [B, H, N, d] and allocate the outputs.
+tensors of shape [B, H, N, d] and allocate the outputs; ``forward_varlen`` /
+``backward_varlen`` take packed [tokens, heads, d] tensors with cumulative
+sequence offsets.
 
 There is no fallback: if ``libfa.so`` has not been built, importing this
 module raises.
@@ -26,8 +29,9 @@ __all__ = [
     "FA_ERR_WORKSPACE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_ARG",
     "MASK_NONE", "MASK_CAUSAL", "MASK_BLOCK_SPARSE", "DTYPE_BF16", "DTYPE_F32",
     "FAError", "fa_fwd", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
-    "fa_bwd_workspace_bytes", "fa_status_string",
-    "forward", "backward", "library_path", "lib",
+    "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen", "fa_bwd_varlen",
+    "fa_bwd_varlen_workspace_bytes",
+    "forward", "backward", "forward_varlen", "backward_varlen", "library_path", "lib",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +81,12 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_dq.restype = i
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
         L.fa_bwd_workspace_bytes.restype = sz
+        L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [i] * 8 + [f, i, i, vp]
+        L.fa_fwd_varlen.restype = i
+        L.fa_bwd_varlen.argtypes = [vp] * 11 + [i] * 8 + [f, i, i, vp, sz, vp]
+        L.fa_bwd_varlen.restype = i
+        L.fa_bwd_varlen_workspace_bytes.argtypes = [i, i, i]
+        L.fa_bwd_varlen_workspace_bytes.restype = sz
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -126,6 +136,25 @@ def fa_bwd_dq(q, k, v, lse, dO, dq, B, H, N, d, scale, mask_kind, block_mask, dt
               workspace, workspace_bytes, stream) -> int:
     return int(lib().fa_bwd_dq(q, k, v, lse, dO, dq, B, H, N, d, ctypes.c_float(scale), mask_kind,
                                block_mask, dtype, workspace, workspace_bytes, stream))
+
+
+def fa_bwd_varlen_workspace_bytes(total_q: int, H: int, d: int) -> int:
+    return int(lib().fa_bwd_varlen_workspace_bytes(total_q, H, d))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, Hkv, max_seqlen_q, max_seqlen_k,
+                  total_q, total_k, d, scale, mask_kind, dtype, stream) -> int:
+    return int(lib().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, Hkv, max_seqlen_q,
+                                   max_seqlen_k, total_q, total_k, d, ctypes.c_float(scale), mask_kind,
+                                   dtype, stream))
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dO, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, H, Hkv, max_seqlen_q,
+                  max_seqlen_k, total_q, total_k, d, scale, mask_kind, dtype, workspace, workspace_bytes,
+                  stream) -> int:
+    return int(lib().fa_bwd_varlen(q, k, v, o, lse, dO, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, H, Hkv,
+                                   max_seqlen_q, max_seqlen_k, total_q, total_k, d, ctypes.c_float(scale),
+                                   mask_kind, dtype, workspace, workspace_bytes, stream))
 
 
 # ---------------------------------------------------------------------------
@@ -228,4 +257,70 @@ def backward(q, k, v, o, lse, do, scale=None, mask_kind=MASK_NONE, block_mask=No
         raise ValueError(f"unknown steps {steps!r}")
     if st != FA_OK:
         raise FAError(st, f"fa_bwd ({steps})")
+    return dq, dk, dv
+
+
+def _check_varlen(q, k, v, cu_q, cu_k):
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [total_q, H, d]; k and v [total_k, Hkv, d]")
+    if k.shape != v.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("k and v must match, and share d with q")
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous bfloat16 GPU tensors")
+    for c in (cu_q, cu_k):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_cuda or not c.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32 GPU tensors")
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None,
+                   mask_kind=MASK_NONE, out=None, lse=None):
+    """Packed-batch forward on the current stream; returns (o, lse).
+
+    q: [total_q, H, d]; k, v: [total_k, Hkv, d] (bf16, H a multiple of Hkv);
+    cu_seqlens_*: int32 [B + 1] device offsets; lse: fp32 [H, total_q].
+    Causal attention aligns each sequence's last query with its last key.
+    """
+    _check_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    Tq, H, d = q.shape
+    Tk, Hkv = k.shape[:2]
+    B = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Hkv, int(max_seqlen_q),
+                       int(max_seqlen_k), Tq, Tk, d, scale, mask_kind, DTYPE_BF16, _stream(q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_varlen")
+    return o, lse
+
+
+def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    scale=None, mask_kind=MASK_NONE, workspace=None, dq=None, dk=None, dv=None):
+    """Packed-batch backward on the current stream; returns (dq, dk, dv)."""
+    _check_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    Tq, H, d = q.shape
+    Tk, Hkv = k.shape[:2]
+    B = cu_seqlens_q.numel() - 1
+    for t in (o, do):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("o and do must match q")
+    if lse.shape != (H, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [H, total_q]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_varlen_workspace_bytes(Tq, H, d), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
+                       cu_seqlens_k.data_ptr(), B, H, Hkv, int(max_seqlen_q), int(max_seqlen_k), Tq, Tk, d,
+                       scale, mask_kind, DTYPE_BF16, workspace.data_ptr(),
+                       workspace.numel() * workspace.element_size(), _stream(q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_varlen")
     return dq, dk, dv

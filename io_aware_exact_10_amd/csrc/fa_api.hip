@@ -49,10 +49,31 @@ fa::AttnParams make_params(int B, int H, int N, int d, float scale, int mask_kin
   p.c = fabsf(scale) * 1.4426950408889634f;
   p.qflip = scale < 0.f ? 0x80008000u : 0u;
   p.block_mask = mask_kind == FA_MASK_BLOCK_SPARSE ? block_mask : nullptr;
+  fa::set_dense_layout(p);
   return p;
 }
 
 }  // namespace
+
+namespace fa {
+
+void set_dense_layout(AttnParams& p) {
+  const int64_t d = p.d, N = p.N, H = p.H;
+  p.Hkv = p.H;
+  p.Nq = p.Nk = p.N;
+  p.Tq = p.Tk = 0;
+  p.cu_q = p.cu_k = nullptr;
+  p.q_rs = p.k_rs = d;
+  p.q_hs = p.k_hs = N * d;
+  p.q_bs = p.k_bs = H * N * d;
+  p.l_hs = N;
+  p.l_bs = H * N;
+  p.rt_rows = (int64_t)p.B * H * N;
+  p.rt_inner = 1;
+  p.rt_hs = 0;
+}
+
+}  // namespace fa
 
 extern "C" {
 
@@ -205,6 +226,139 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, con
   const int st = bwd_prepare(q, k, v, unused, lse, dO, dq, unused, unused, B, H, N, d, scale, mask_kind, block_mask,
                              dtype, workspace, workspace_bytes, &p);
   return st != FA_OK ? st : bwd_launch(p, mask_kind, dtype, fa::kBwdDq, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// packed variable-length batches with shared K/V heads (bf16)
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kMaxHeads = 1 << 16;   // keeps a 64-row tile's byte offsets in 32 bits
+
+int varlen_check(int B, int H, int Hkv, int max_q, int max_k, int total_q, int total_k, int d, float scale,
+                 int mask_kind, int dtype) {
+  if (B < 1 || H < 1 || Hkv < 1 || max_q < 1 || max_k < 1 || total_q < 1 || total_k < 1) return FA_ERR_SHAPE;
+  if (H > kMaxHeads || H % Hkv != 0) return FA_ERR_SHAPE;
+  if ((int64_t)total_q * H > kMaxElems / 128 || (int64_t)total_k * Hkv > kMaxElems / 128) return FA_ERR_SHAPE;
+  if ((int64_t)B * H * (((int64_t)max_q + 63) / 64) >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  if ((int64_t)B * Hkv * (((int64_t)max_k + 63) / 64) >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_ERR_ARG;
+  if (mask_kind == FA_MASK_BLOCK_SPARSE) return FA_ERR_MASK;
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL) return FA_ERR_MASK;
+  return FA_OK;
+}
+
+fa::AttnParams varlen_params(const int* cu_q, const int* cu_k, int B, int H, int Hkv, int max_q, int max_k,
+                             int total_q, int total_k, int d, float scale) {
+  fa::AttnParams p = {};
+  p.B = B;
+  p.H = H;
+  p.N = max_q;
+  p.d = d;
+  p.scale = scale;
+  p.c = fabsf(scale) * 1.4426950408889634f;
+  p.qflip = scale < 0.f ? 0x80008000u : 0u;
+  p.Hkv = Hkv;
+  p.Nq = max_q;
+  p.Nk = max_k;
+  p.Tq = total_q;
+  p.Tk = total_k;
+  p.cu_q = cu_q;
+  p.cu_k = cu_k;
+  p.q_rs = (int64_t)H * d;
+  p.q_hs = d;
+  p.k_rs = (int64_t)Hkv * d;
+  p.k_hs = d;
+  p.l_hs = total_q;
+  p.rt_rows = (int64_t)total_q * H;
+  p.rt_inner = H;
+  p.rt_hs = total_q;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_varlen_workspace_bytes(int total_q, int H, int d) {
+  if (total_q < 1 || H < 1 || (d != 64 && d != 128)) return 0;
+  return ((size_t)total_q * (size_t)H * sizeof(float) + 255) & ~(size_t)255;
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int B, int H, int Hkv, int max_seqlen_q, int max_seqlen_k,
+                  int total_q, int total_k, int d, float scale, int mask_kind,
+                  int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  int st = varlen_check(B, H, Hkv, max_seqlen_q, max_seqlen_k, total_q, total_k, d, scale, mask_kind, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return FA_ERR_ALIGN;
+  const size_t qb = (size_t)total_q * H * d * 2, kb = (size_t)total_k * Hkv * d * 2;
+  const size_t lb = (size_t)total_q * H * sizeof(float), cb = (size_t)(B + 1) * sizeof(int);
+  const void* ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
+  const size_t insz[5] = {qb, kb, kb, cb, cb};
+  for (int j = 0; j < 5; ++j)
+    if (overlap(o, qb, ins[j], insz[j]) || overlap(lse, lb, ins[j], insz[j])) return FA_ERR_ARG;
+  if (overlap(o, qb, lse, lb)) return FA_ERR_ARG;
+  fa::AttnParams p = varlen_params(cu_seqlens_q, cu_seqlens_k, B, H, Hkv, max_seqlen_q, max_seqlen_k, total_q,
+                                   total_k, d, scale);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  return fa::launch_fwd_bf16(p, mask_kind, stream) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dO, void* dq, void* dk, void* dv,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int B, int H, int Hkv, int max_seqlen_q, int max_seqlen_k,
+                  int total_q, int total_k, int d, float scale, int mask_kind, int dtype,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k)
+    return FA_ERR_NULL;
+  int st = varlen_check(B, H, Hkv, max_seqlen_q, max_seqlen_k, total_q, total_k, d, scale, mask_kind, dtype);
+  if (st != FA_OK) return st;
+  const size_t need = fa_bwd_varlen_workspace_bytes(total_q, H, d);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void* tens[8] = {q, k, v, o, dO, dq, dk, dv};
+  for (const void* t : tens)
+    if (!aligned(t, 16)) return FA_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
+  const size_t qb = (size_t)total_q * H * d * 2, kb = (size_t)total_k * Hkv * d * 2;
+  const size_t lb = (size_t)total_q * H * sizeof(float), cb = (size_t)(B + 1) * sizeof(int);
+  const void* ins[8] = {q, k, v, o, dO, lse, cu_seqlens_q, cu_seqlens_k};
+  const size_t insz[8] = {qb, kb, kb, qb, qb, lb, cb, cb};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const size_t outsz[4] = {qb, kb, kb, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ARG;
+  }
+  fa::AttnParams p = varlen_params(cu_seqlens_q, cu_seqlens_k, B, H, Hkv, max_seqlen_q, max_seqlen_k, total_q,
+                                   total_k, d, scale);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = const_cast<void*>(o);
+  p.lse = const_cast<float*>(lse);
+  p.dO = dO;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dterm = (float*)workspace;
+  return fa::launch_bwd_bf16(p, mask_kind, fa::kBwdAll, stream) == 0 ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

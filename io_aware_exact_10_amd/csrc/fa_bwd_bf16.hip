@@ -46,8 +46,9 @@ constexpr int kMaskBlk = 128;
 // row term D = rowsum(dO * O), fp32 accumulation
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_rowterm_bf16_kernel(AttnParams p, size_t rows) {
+__global__ __launch_bounds__(kThreads) void bwd_rowterm_bf16_kernel(AttnParams p) {
   constexpr int DC = D / 8;
+  const size_t rows = (size_t)p.rt_rows;
   const size_t gt = (size_t)blockIdx.x * kThreads + threadIdx.x;
   const size_t row = gt / DC;
   const int col = (int)(gt % DC);
@@ -63,7 +64,10 @@ __global__ __launch_bounds__(kThreads) void bwd_rowterm_bf16_kernel(AttnParams p
   }
 #pragma unroll
   for (int off = DC / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && col == 0) p.dterm[row] = acc;
+  if (row < rows && col == 0) {
+    const size_t inner = (size_t)p.rt_inner;
+    p.dterm[(row % inner) * (size_t)p.rt_hs + row / inner] = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -89,28 +93,41 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   constexpr int NDT = D / 32;
   constexpr int QPB = kMaskBlk / kDkvBQ;               // query tiles per mask block
 
-  const int N = p.N;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
   const uint32_t L = xcd_remap(blockIdx.x, total);
-  const uint32_t bh = L / nkt;
+  const uint32_t bh = L / nkt;                 // (batch, K/V head)
   const int kt = (int)(L - bh * nkt);
   const int k0 = kt * kDkvBK;
+  const int bat = (int)bh / p.Hkv, hk = (int)bh - bat * p.Hkv;
+  const SeqView sq = seq_view(p, bat);
+  if (k0 >= sq.nk) return;                     // past this sequence's keys (packed batches)
+  const int Nq = sq.nq, Nk = sq.nk;
+  const int off = Nk - Nq;                     // causal: key j visible to query i iff j <= i + off
+  const int G = p.H / p.Hkv;                   // query heads sharing this K/V head
   const int kw0 = k0 + 32 * w;
   const int kj = kw0 + r;
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ Qh = (const uint16_t*)p.q + hoff;
-  const uint16_t* __restrict__ Kh = (const uint16_t*)p.k + hoff;
-  const uint16_t* __restrict__ Vh = (const uint16_t*)p.v + hoff;
-  const uint16_t* __restrict__ dOh = (const uint16_t*)p.dO + hoff;
-  const float* __restrict__ lseh = p.lse + (size_t)bh * N;
-  const float* __restrict__ dth = p.dterm + (size_t)bh * N;
+  const uint16_t* __restrict__ Kh = (const uint16_t*)p.k + sq.kb + hk * p.k_hs;
+  const uint16_t* __restrict__ Vh = (const uint16_t*)p.v + sq.kb + hk * p.k_hs;
+  const int64_t k_rs = p.k_rs;
+  // Query head hk * G + j: its Q / dO rows and its LSE / row-term entries.
+  const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + sq.qb + (int64_t)hk * G * p.q_hs;
+  const uint16_t* __restrict__ dOg = (const uint16_t*)p.dO + sq.qb + (int64_t)hk * G * p.q_hs;
+  const float* __restrict__ lseg = p.lse + sq.lb + (int64_t)hk * G * p.l_hs;
+  const float* __restrict__ dtg = p.dterm + sq.lb + (int64_t)hk * G * p.l_hs;
 
-  const int nqt = (N + kDkvBQ - 1) / kDkvBQ;
-  const int qbeg = MASK == 1 ? k0 / kDkvBQ : 0;
+  const int nqt = (Nq + kDkvBQ - 1) / kDkvBQ;
+  int qbeg = 0;
+  if (MASK == 1) {
+    const int first = k0 - off;                // first query that sees key k0
+    qbeg = first <= 0 ? 0 : min(nqt, first / kDkvBQ);
+  }
   MaskScan ms;
   if (MASK == 2) ms.init(p.block_mask + kt, p.nblk, p.nblk);   // column kt of the mask
-  auto next_tile = [&](int it) -> int {
+  // The loop runs over (query head j, query tile it) pairs, coded as
+  // j * nqt + it; code nend means done.
+  const int nend = G * nqt;
+  auto next_in_head = [&](int it) -> int {
     if (MASK != 2 || it >= nqt) return it < nqt ? it : nqt;
     const int blk = it / QPB;
     const int nb = ms.next(blk);
@@ -118,30 +135,40 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     const int t = nb == blk ? it : nb * QPB;
     return t < nqt ? t : nqt;
   };
+  auto next_tile = [&](int code) -> int {
+    int j = code / nqt, it = code - j * nqt;
+    if (j >= G) return nend;
+    it = next_in_head(it < qbeg ? qbeg : it);
+    if (it < nqt) return j * nqt + it;
+    // the visible query tiles are the same in every head
+    it = next_in_head(qbeg);
+    return it < nqt && j + 1 < G ? (j + 1) * nqt + it : nend;
+  };
   TileLoader<D, kDkvBQ, 4> ld;
-  ld.init(w, lane);
-  auto issue = [&](int it, int buf) {
+  ld.init(w, lane, (int)(p.q_rs * 2));
+  auto issue = [&](int code, int buf) {
+    const int j = code / nqt, it = code - j * nqt;
     const int q0 = it * kDkvBQ;
-    ld.load(sm.q[buf], Qh, q0, N);
-    ld.load(sm.dO[buf], dOh, q0, N);
+    ld.load(sm.q[buf], Qg + j * p.q_hs, q0, Nq);
+    ld.load(sm.dO[buf], dOg + j * p.q_hs, q0, Nq);
     if (w < 2) {   // one dword per lane: 64 row statistics per tile
-      const int q = min(q0 + lane, N - 1);
-      const float* src = w == 0 ? lseh + q : dth + q;
+      const int q = min(q0 + lane, Nq - 1);
+      const float* src = (w == 0 ? lseg : dtg) + j * p.l_hs + q;
       float* dst = w == 0 ? sm.lse[buf] : sm.dterm[buf];
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 4, 0, 0);
     }
   };
 
-  int it = next_tile(qbeg);
-  if (it < nqt) issue(it, 0);
+  int it = nqt > 0 ? next_tile(0) : nend;
+  if (it < nend) issue(it, 0);
 
   u32x4 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (kj < N) {
-      a = *(const u32x4*)(Kh + (size_t)kj * D + ks * 16 + h * 8);
-      b = *(const u32x4*)(Vh + (size_t)kj * D + ks * 16 + h * 8);
+    if (kj < Nk) {
+      a = *(const u32x4*)(Kh + kj * k_rs + ks * 16 + h * 8);
+      b = *(const u32x4*)(Vh + kj * k_rs + ks * 16 + h * 8);
     }
     kf[ks] = a ^ p.qflip;   // S = |scale| Q (sign(scale) K)^T: the sign of scale rides on K here
     vf[ks] = b;
@@ -163,9 +190,8 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   //   dV, dK of block 1.
   // NM selects the masked variant (diagonal and tail tiles only); in the
   // unmasked one both sub-blocks are live and the stages are straight-line.
-  auto tile = [&](int buf, int it, auto nm) {
+  auto tile = [&](int buf, int q0, auto nm) {
     constexpr bool NM = decltype(nm)::value;
-    const int q0 = it * kDkvBQ;
     // Per-tile lane addresses relative to the shared block (see the
     // forward kernel): one XOR per fragment, opaque so they are not all
     // kept live across the loop.
@@ -176,7 +202,7 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     asm volatile("" : "+v"(qr), "+v"(orow), "+v"(qc0), "+v"(qc1), "+v"(oc0), "+v"(oc1));
     bool live[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) live[mb] = !NM || !(MASK == 1 && q0 + 32 * mb + 31 < kw0);
+    for (int mb = 0; mb < 2; ++mb) live[mb] = !NM || !(MASK == 1 && q0 + 32 * mb + 31 + off < kw0);
 
     auto sdp = [&](int mb, f32x16& sv, f32x16& dpv) {
       sv = zero16();
@@ -207,7 +233,7 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
             float pp = fast_exp2(__builtin_fmaf(sv[i], c, -lv[e] * kLog2e));
             if (NM) {
               const int q = q0 + ql + e;
-              if (q >= N || (MASK == 1 && kj > q)) pp = 0.f;
+              if (q >= Nq || (MASK == 1 && kj > q + off)) pp = 0.f;
             }
             pv[4 * g2 + e] = pp;
             dv[4 * g2 + e] = pp * (dpv[i] - dd[e]);
@@ -252,21 +278,21 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
       }
     }
   };
-  auto compute = [&](int buf, int it) {
-    const int q0 = it * kDkvBQ;
-    const bool needm = (MASK == 1 && q0 < kw0 + 31) || q0 + kDkvBQ > N;
+  auto compute = [&](int buf, int code) {
+    const int q0 = (code % nqt) * kDkvBQ;
+    const bool needm = (MASK == 1 && q0 + off < kw0 + 31) || q0 + kDkvBQ > Nq;
     if (needm)
-      tile(buf, it, std::true_type{});
+      tile(buf, q0, std::true_type{});
     else
-      tile(buf, it, std::false_type{});
+      tile(buf, q0, std::false_type{});
   };
 
   wait_vmem();
   __syncthreads();
   int buf = 0;
-  while (it < nqt) {
+  while (it < nend) {
     const int itn = next_tile(it + 1);
-    if (itn < nqt) issue(itn, buf ^ 1);
+    if (itn < nend) issue(itn, buf ^ 1);
     compute(buf, it);
     wait_vmem();
     __syncthreads();
@@ -274,10 +300,10 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     it = itn;
   }
 
-  if (kj < N) {
+  if (kj < Nk) {
     const float sk = p.scale;   // dK = scale dS^T Q (Q unmodified; the sign of scale only entered S via kf)
-    uint16_t* __restrict__ dKrow = (uint16_t*)p.dk + hoff + (size_t)kj * D;
-    uint16_t* __restrict__ dVrow = (uint16_t*)p.dv + hoff + (size_t)kj * D;
+    uint16_t* __restrict__ dKrow = (uint16_t*)p.dk + sq.kb + hk * p.k_hs + kj * k_rs;
+    uint16_t* __restrict__ dVrow = (uint16_t*)p.dv + sq.kb + hk * p.k_hs + kj * k_rs;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -316,7 +342,6 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   constexpr int NDT = D / 32;
   constexpr int TPB = kMaskBlk / kDqBK;
 
-  const int N = p.N;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
   const uint32_t L = xcd_remap(blockIdx.x, total);
@@ -324,17 +349,26 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   uint32_t qt = L - bh * nqt;
   if (MASK == 1) qt = nqt - 1 - qt;
   const int q0 = (int)qt * kDqBQ;
+  const int bat = (int)bh / p.H, hq = (int)bh - bat * p.H;
+  const SeqView sq = seq_view(p, bat);
+  if (q0 >= sq.nq) return;                     // past this sequence's queries (packed batches)
+  const int Nq = sq.nq, Nk = sq.nk;
+  const int off = Nk - Nq;                     // causal: key j visible to query i iff j <= i + off
+  const int hk = hq / (p.H / p.Hkv);
   const int qw0 = q0 + 32 * w;
   const int qi = qw0 + r;
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ Qh = (const uint16_t*)p.q + hoff;
-  const uint16_t* __restrict__ Kh = (const uint16_t*)p.k + hoff;
-  const uint16_t* __restrict__ Vh = (const uint16_t*)p.v + hoff;
-  const uint16_t* __restrict__ dOh = (const uint16_t*)p.dO + hoff;
+  const int64_t q_rs = p.q_rs;
+  const uint16_t* __restrict__ Qh = (const uint16_t*)p.q + sq.qb + hq * p.q_hs;
+  const uint16_t* __restrict__ dOh = (const uint16_t*)p.dO + sq.qb + hq * p.q_hs;
+  const uint16_t* __restrict__ Kh = (const uint16_t*)p.k + sq.kb + hk * p.k_hs;
+  const uint16_t* __restrict__ Vh = (const uint16_t*)p.v + sq.kb + hk * p.k_hs;
 
-  const int nkt = (N + kDqBK - 1) / kDqBK;
+  const int nkt = (Nk + kDqBK - 1) / kDqBK;
   int kend = nkt;
-  if (MASK == 1) kend = min(nkt, (q0 + kDqBQ + kDqBK - 1) / kDqBK);
+  if (MASK == 1) {
+    const int last = q0 + kDqBQ - 1 + off;     // last key any row of the tile sees
+    kend = last < 0 ? 0 : min(nkt, last / kDqBK + 1);
+  }
   MaskScan ms;
   if (MASK == 2) ms.init(p.block_mask + (size_t)qt * p.nblk, 1, p.nblk);
   auto next_tile = [&](int kt) -> int {
@@ -346,10 +380,10 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     return t < kend ? t : kend;
   };
   TileLoader<D, kDqBK, 4> ld;
-  ld.init(w, lane);
+  ld.init(w, lane, (int)(p.k_rs * 2));
   auto issue = [&](int kt, int buf) {
-    ld.load_recompute(sm.k[buf], Kh, kt * kDqBK, N);
-    ld.load(sm.v[buf], Vh, kt * kDqBK, N);
+    ld.load_recompute(sm.k[buf], Kh, kt * kDqBK, Nk);
+    ld.load(sm.v[buf], Vh, kt * kDqBK, Nk);
   };
 
   int kt = next_tile(0);
@@ -359,18 +393,19 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (qi < N) {
-      a = *(const u32x4*)(Qh + (size_t)qi * D + ks * 16 + h * 8);
-      b = *(const u32x4*)(dOh + (size_t)qi * D + ks * 16 + h * 8);
+    if (qi < Nq) {
+      a = *(const u32x4*)(Qh + qi * q_rs + ks * 16 + h * 8);
+      b = *(const u32x4*)(dOh + qi * q_rs + ks * 16 + h * 8);
     }
     qf[ks] = a ^ p.qflip;
     of[ks] = b;
   }
   float lse2 = INFINITY, dti = 0.f;
-  if (qi < N) {
-    const float l = p.lse[(size_t)bh * N + qi];
+  if (qi < Nq) {
+    const int64_t li = sq.lb + hq * p.l_hs + qi;
+    const float l = p.lse[li];
     lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-    dti = p.dterm[(size_t)bh * N + qi];
+    dti = p.dterm[li];
   }
 
   f32x16 dqT[NDT];
@@ -392,7 +427,7 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     asm volatile("" : "+v"(kr), "+v"(vr), "+v"(kc0), "+v"(kc1));
     bool live[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) live[kb] = !NM || !(MASK == 1 && k0 + kb * 32 > qw0 + 31);
+    for (int kb = 0; kb < 2; ++kb) live[kb] = !NM || !(MASK == 1 && k0 + kb * 32 > qw0 + 31 + off);
 
     auto sdp = [&](int kb, f32x16& sv, f32x16& dpv) {
       sv = zero16();
@@ -414,7 +449,7 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
           float pp = fast_exp2(__builtin_fmaf(sv[i], c, -lse2));
           if (NM) {
             const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (key >= N || (MASK == 1 && key > qi)) pp = 0.f;
+            if (key >= Nk || (MASK == 1 && key > qi + off)) pp = 0.f;
           }
           y[e] = pp * (dpv[i] - dti);
         }
@@ -454,8 +489,8 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   };
   auto compute = [&](int buf, int kt) {
     const int k0 = kt * kDqBK;
-    if (MASK == 1 && k0 > qw0 + 31) return;
-    const bool need_mask = (k0 + kDqBK > N) || (MASK == 1 && k0 + kDqBK - 1 > qw0);
+    if (MASK == 1 && k0 > qw0 + 31 + off) return;   // whole tile past this wave's diagonal
+    const bool need_mask = (k0 + kDqBK > Nk) || (MASK == 1 && k0 + kDqBK - 1 > qw0 + off);
     if (need_mask)
       tile(buf, kt, std::true_type{});
     else
@@ -475,9 +510,11 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     kt = ktn;
   }
 
-  if (qi < N) {
+  if (qi < Nq) {
     const float sc = p.scale;   // dQ = scale dS K (K unmodified; the sign of scale only entered S via qf)
-    uint16_t* __restrict__ dQrow = (uint16_t*)p.dq + hoff + (size_t)qi * D;
+    int qe = qi;                // opaque: the row offset is recomputed here, not kept live across the loop
+    asm volatile("" : "+v"(qe));
+    uint16_t* __restrict__ dQrow = (uint16_t*)p.dq + sq.qb + hq * p.q_hs + qe * q_rs;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -496,26 +533,24 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 template <int D, int MASK>
 static int launch_bwd_t(const AttnParams& p, int steps, hipStream_t stream) {
   AttnParams pp = p;
-  const size_t rows = (size_t)p.B * p.H * p.N;
   if (steps & kBwdRowterm) {
-    const size_t threads = rows * (D / 8);
+    const size_t threads = (size_t)p.rt_rows * (D / 8);
     const uint32_t grid = (uint32_t)((threads + kThreads - 1) / kThreads);
-    size_t rr = rows;
-    void* args[] = {&pp, &rr};
+    void* args[] = {&pp};
     hipError_t e = hipLaunchKernel((const void*)&bwd_rowterm_bf16_kernel<D>, dim3(grid), dim3(kThreads),
                                    args, 0, stream);
     if (e != hipSuccess) return (int)e;
   }
   if (steps & kBwdDkdv) {
-    uint32_t nkt = (uint32_t)((p.N + kDkvBK - 1) / kDkvBK);
-    uint32_t total = nkt * (uint32_t)p.B * (uint32_t)p.H;
+    uint32_t nkt = (uint32_t)((p.Nk + kDkvBK - 1) / kDkvBK);
+    uint32_t total = nkt * (uint32_t)p.B * (uint32_t)p.Hkv;
     void* args[] = {&pp, &nkt, &total};
     hipError_t e = hipLaunchKernel((const void*)&bwd_dkdv_bf16_kernel<D, MASK>, dim3(total), dim3(kThreads),
                                    args, 0, stream);
     if (e != hipSuccess) return (int)e;
   }
   if (steps & kBwdDq) {
-    uint32_t nqt = (uint32_t)((p.N + kDqBQ - 1) / kDqBQ);
+    uint32_t nqt = (uint32_t)((p.Nq + kDqBQ - 1) / kDqBQ);
     uint32_t total = nqt * (uint32_t)p.B * (uint32_t)p.H;
     void* args[] = {&pp, &nqt, &total};
     hipError_t e = hipLaunchKernel((const void*)&bwd_dq_bf16_kernel<D, MASK>, dim3(total), dim3(kThreads),

@@ -86,14 +86,15 @@ __device__ __forceinline__ int tile_off(int r, int col) {
   return r * (D * 2) + ((((col >> 3) ^ swz<D>(r))) << 4) + ((col & 7) << 1);
 }
 
-// Asynchronous copy of rows [r0, r0 + ROWS) of a [N, D] bf16 matrix into a
-// swizzled LDS tile, straight from global memory to LDS (no registers).
-// Each wave instruction fills one contiguous KiB: lane i writes bytes
-// [16 i, 16 i + 16), so lane i fetches the global chunk that belongs there.
-// The byte offset of that chunk from the tile's first row does not depend on
-// the tile, so it is computed once per lane (offs); a full tile is then one
-// uniform base pointer plus offs[i] per instruction. Rows past N (only in
-// the last tile) read row N - 1: finite data the callers mask or ignore.
+// Asynchronous copy of rows [r0, r0 + ROWS) of an N-row bf16 matrix with D
+// columns and a row stride of rsb bytes into a swizzled LDS tile, straight
+// from global memory to LDS (no registers). Each wave instruction fills one
+// contiguous KiB: lane i writes bytes [16 i, 16 i + 16), so lane i fetches
+// the global chunk that belongs there. The byte offset of that chunk from the
+// tile's first row does not depend on the tile, so it is computed once per
+// lane (offs); a full tile is then one uniform base pointer plus offs[i] per
+// instruction. Rows past N (only in the last tile) read row N - 1: finite
+// data the callers mask or ignore.
 // Completion: s_waitcnt vmcnt(0) then a workgroup barrier.
 template <int D, int ROWS, int NWAVES>
 struct TileLoader {
@@ -103,18 +104,20 @@ struct TileLoader {
   static constexpr int PER = NK / NWAVES;      // pieces per wave
   static_assert(NK % NWAVES == 0, "tile pieces per wave");
   int offs[PER];                               // bytes from the tile's first row
-  int wave, lane_;
+  int wave, lane_, rsb;
 
-  __device__ __forceinline__ static int offset(int w, int lane, int i) {
-    const int ci = w + i * NWAVES;
-    const int row = ci * RPK + lane / CPR;
-    return row * (2 * D) + (((lane % CPR) ^ swz<D>(row)) << 4);
+  __device__ __forceinline__ static int row_of(int w, int lane, int i) {
+    return (w + i * NWAVES) * RPK + lane / CPR;
   }
-  __device__ __forceinline__ void init(int w, int lane) {
+  __device__ __forceinline__ static int chunk_of(int w, int lane, int i) {
+    return (lane % CPR) ^ swz<D>(row_of(w, lane, i));
+  }
+  __device__ __forceinline__ void init(int w, int lane, int row_bytes) {
     wave = w;
     lane_ = lane;
+    rsb = row_bytes;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) offs[i] = offset(w, lane, i);
+    for (int i = 0; i < PER; ++i) offs[i] = row_of(w, lane, i) * rsb + (chunk_of(w, lane, i) << 4);
   }
   // Same as load() with the offsets recomputed at the call (no registers kept
   // live across the loop), for kernels short of VGPRs.
@@ -122,23 +125,21 @@ struct TileLoader {
     int l = lane_;
     asm volatile("" : "+v"(l));
 #pragma unroll
-    for (int i = 0; i < PER; ++i) offs[i] = offset(wave, l, i);
+    for (int i = 0; i < PER; ++i) offs[i] = row_of(wave, l, i) * rsb + (chunk_of(wave, l, i) << 4);
     load(tile, X, r0, N);
   }
   __device__ __forceinline__ void load(uint8_t* tile, const uint16_t* __restrict__ X, int r0, int N) const {
-    const uint8_t* base = (const uint8_t*)(X + (size_t)r0 * D);
+    const uint8_t* base = (const uint8_t*)X + (int64_t)r0 * rsb;
     if (r0 + ROWS <= N) {
 #pragma unroll
       for (int i = 0; i < PER; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(base + offs[i]), (lds_void*)(tile + (wave + i * NWAVES) * 1024),
                                          16, 0, 0);
     } else {
-      const int last = (N - 1 - r0) * (2 * D);   // first byte of row N - 1, relative to row r0
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         int o = offs[i];
-        const int row_off = o & ~(2 * D - 1);
-        if (row_off > last) o = last + (o & (2 * D - 1));
+        if (r0 + row_of(wave, lane_, i) >= N) o = (N - 1 - r0) * rsb + (chunk_of(wave, lane_, i) << 4);
         __builtin_amdgcn_global_load_lds((const void*)(base + o), (lds_void*)(tile + (wave + i * NWAVES) * 1024),
                                          16, 0, 0);
       }

@@ -70,7 +70,6 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   constexpr int TPB = kMaskBlock / kFwdBC;                 // key tiles per mask block
   constexpr int NDT = D / 32;                              // 32-row blocks of O^T
 
-  const int N = p.N;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
 
@@ -79,16 +78,25 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   uint32_t qt = L - bh * nqt;
   if (MASK == 1) qt = nqt - 1 - qt;            // causal: longest rows first
   const int q0 = (int)qt * kFwdBR;
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ Qh = (const uint16_t*)p.q + hoff;
-  const uint16_t* __restrict__ Kh = (const uint16_t*)p.k + hoff;
-  const uint16_t* __restrict__ Vh = (const uint16_t*)p.v + hoff;
+  const int bat = (int)bh / p.H, hq = (int)bh - bat * p.H;
+  const SeqView sq = seq_view(p, bat);
+  if (q0 >= sq.nq) return;                     // past this sequence's queries (packed batches)
+  const int Nq = sq.nq, Nk = sq.nk;
+  const int off = Nk - Nq;                     // causal: key j visible to query i iff j <= i + off
+  const int hk = hq / (p.H / p.Hkv);
+  const uint16_t* __restrict__ Qh = (const uint16_t*)p.q + sq.qb + hq * p.q_hs;
+  const uint16_t* __restrict__ Kh = (const uint16_t*)p.k + sq.kb + hk * p.k_hs;
+  const uint16_t* __restrict__ Vh = (const uint16_t*)p.v + sq.kb + hk * p.k_hs;
+  const int64_t q_rs = p.q_rs;
   const int qw0 = q0 + w * 32;
   const int qi = qw0 + r;
 
-  const int nkt = (N + kFwdBC - 1) / kFwdBC;
+  const int nkt = (Nk + kFwdBC - 1) / kFwdBC;
   int kend = nkt;
-  if (MASK == 1) kend = min(nkt, (q0 + kFwdBR + kFwdBC - 1) / kFwdBC);
+  if (MASK == 1) {
+    const int last = q0 + kFwdBR - 1 + off;    // last key any row of the tile sees
+    kend = last < 0 ? 0 : min(nkt, last / kFwdBC + 1);
+  }
   MaskScan ms;
   if (MASK == 2) ms.init(p.block_mask + (size_t)qt * p.nblk, 1, p.nblk);
   auto next_tile = [&](int kt) -> int {
@@ -100,10 +108,10 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     return t < kend ? t : kend;
   };
   TileLoader<D, kFwdBC, NW> ld;
-  ld.init(w, lane);
+  ld.init(w, lane, (int)(p.k_rs * 2));
   auto issue = [&](int kt, int buf) {
-    ld.load(sm.k[buf], Kh, kt * kFwdBC, N);
-    ld.load(sm.v[buf], Vh, kt * kFwdBC, N);
+    ld.load(sm.k[buf], Kh, kt * kFwdBC, Nk);
+    ld.load(sm.v[buf], Vh, kt * kFwdBC, Nk);
   };
   const int kbase_l = row_frag_base<D>(lane);
   const int vbase0_l = col_frag_base<D>(lane, 0), vbase1_l = col_frag_base<D>(lane, 1);
@@ -116,7 +124,7 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < N) x = *(const u32x4*)(Qh + (size_t)qi * D + ks * 16 + h * 8);
+    if (qi < Nq) x = *(const u32x4*)(Qh + qi * q_rs + ks * 16 + h * 8);
     qf[ks] = x ^ p.qflip;
   }
 
@@ -145,7 +153,7 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     int kbase = kbase_l + (int)(sm.k[buf] - sbase);
     int vbase0 = vbase0_l + (int)(sm.v[buf] - sbase), vbase1 = vbase1_l + (int)(sm.v[buf] - sbase);
     asm volatile("" : "+v"(kbase), "+v"(vbase0), "+v"(vbase1));
-    const bool live1 = !(MASK == 1 && k0 + 32 > qw0 + 31);
+    const bool live1 = !(MASK == 1 && k0 + 32 > qw0 + 31 + off);
 
     u32x4 kf[D / 16];
 #pragma unroll
@@ -165,7 +173,7 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        const bool vis = live && key < N && (MASK != 1 || key <= qi);
+        const bool vis = live && key < Nk && (MASK != 1 || key <= qi + off);
         sv[i] = vis ? sv[i] * c : -INFINITY;
       }
     };
@@ -185,7 +193,9 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     // Raise the reference max only when some row of the wave outgrows it.
     if (__ballot(mx > m_run + kRescaleThreshold)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);   // 0 on the first update
+      // 0 on a row's first update; 1 for a row that has seen no key yet
+      // (-inf on both sides) while others in the wave raise theirs.
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -234,8 +244,8 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   };
   auto compute = [&](int buf, int kt) {
     const int k0 = kt * kFwdBC;
-    if (MASK == 1 && k0 > qw0 + 31) return;      // whole tile above this wave's diagonal
-    const bool need_mask = (k0 + kFwdBC > N) || (MASK == 1 && k0 + kFwdBC - 1 > qw0);
+    if (MASK == 1 && k0 > qw0 + 31 + off) return;   // whole tile past this wave's diagonal
+    const bool need_mask = (k0 + kFwdBC > Nk) || (MASK == 1 && k0 + kFwdBC - 1 > qw0 + off);
     if (need_mask)
       tile(buf, kt, std::true_type{});
     else
@@ -258,8 +268,8 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   // Epilogue: combine the two lane halves' partial sums, normalise, store.
   const float lt = l_run + __shfl_xor(l_run, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (qi < N) {
-    uint16_t* __restrict__ Orow = (uint16_t*)p.o + hoff + (size_t)qi * D;
+  if (qi < Nq) {
+    uint16_t* __restrict__ Orow = (uint16_t*)p.o + sq.qb + hq * p.q_hs + qi * q_rs;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -269,14 +279,14 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
                      pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
         *(u32x2*)(Orow + dd) = val;
       }
-    if (h == 0) p.lse[(size_t)bh * N + qi] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+    if (h == 0) p.lse[sq.lb + hq * p.l_hs + qi] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
 template <int D, int MASK>
 static int launch_fwd_t(const AttnParams& p, hipStream_t stream) {
   using S = FwdShape<D, MASK>;
-  const uint32_t nqt = (uint32_t)((p.N + S::BR - 1) / S::BR);
+  const uint32_t nqt = (uint32_t)((p.Nq + S::BR - 1) / S::BR);
   const uint32_t total = nqt * (uint32_t)p.B * (uint32_t)p.H;
   AttnParams pp = p;
   void* args[] = {&pp, (void*)&nqt, (void*)&total};

@@ -143,3 +143,69 @@ def make_inputs(w: Workload, seed: int | None = None, with_do: bool | None = Non
 def small_workload(B, H, N, d, dtype=DTYPE_BF16, mask_kind=MASK_NONE, seed=0, backward=True):
     """A workload of arbitrary shape for parity cases (ragged N, tiny B, H)."""
     return Workload(f"B{B}H{H}N{N}d{d}", B, H, N, d, dtype, mask_kind, backward, seed)
+
+
+# ---------------------------------------------------------------------------
+# packed variable-length batches (tokens of all sequences back to back)
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class PackedInputs:
+    """A packed batch: q, do [total_q, H, d]; k, v [total_k, Hkv, d].
+
+    ``cu_q`` / ``cu_k`` are the int32 cumulative offsets (B + 1 entries);
+    tokens past ``cu_q[-1]`` / ``cu_k[-1]`` (``pad_q`` / ``pad_k`` of them)
+    belong to no sequence. Values are bf16-rounded fp32 as in ``Inputs``.
+    """
+    lens_q: list
+    lens_k: list
+    H: int
+    Hkv: int
+    d: int
+    seed: int
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray
+    q_bits: np.ndarray
+    k_bits: np.ndarray
+    v_bits: np.ndarray
+    do_bits: np.ndarray
+
+    @property
+    def B(self) -> int:
+        return len(self.lens_q)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def name(self) -> str:
+        return f"packed B{self.B} H{self.H}/{self.Hkv} d{self.d} Tq{self.q.shape[0]} Tk{self.k.shape[0]}"
+
+
+def offsets(lens) -> np.ndarray:
+    """int32 [len(lens) + 1] cumulative token offsets starting at 0."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lens, dtype=np.int64))]).astype(np.int32)
+
+
+def packed_inputs(lens_q, lens_k, H, Hkv, d, seed, pad_q=0, pad_k=0) -> PackedInputs:
+    """Draw a packed bf16 batch: Q, K, V, dO in that order from ``seed``."""
+    cu_q, cu_k = offsets(lens_q), offsets(lens_k)
+    tq, tk = int(cu_q[-1]) + pad_q, int(cu_k[-1]) + pad_k
+    rng = np.random.default_rng(seed)
+    draws = [rng.standard_normal(s, dtype=np.float32) for s in ((tq, H, d), (tk, Hkv, d), (tk, Hkv, d), (tq, H, d))]
+    bits = [bf16_bits(a) for a in draws]
+    vals = [bf16_to_f32(b) for b in bits]
+    return PackedInputs(list(lens_q), list(lens_k), H, Hkv, d, seed, cu_q, cu_k, *vals, *bits)
+
+
+def length_mix(B: int, max_len: int, seed: int, min_len: int = 1) -> list:
+    """B sequence lengths drawn uniformly from [min_len, max_len], one of them
+    pinned to max_len so the batch reaches its stated maximum."""
+    rng = np.random.default_rng(200 + seed)
+    lens = rng.integers(min_len, max_len + 1, size=B).tolist()
+    lens[int(rng.integers(0, B))] = max_len
+    return lens

@@ -47,7 +47,8 @@ def call_bwd(**kw):
 def test_library_exports_every_declared_symbol():
     names = fa.declared_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
-                          "fa_bwd_workspace_bytes", "fa_status_string"}
+                          "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen",
+                          "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes"}
     L = fa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -181,3 +182,78 @@ def test_bwd_step_validation(name):
         assert f(**step_args(name, lse=4 * BIG + A + 1)) == fa.FA_ERR_ALIGN
     else:
         assert f(**step_args(name, workspace=A + 3 * BIG)) == fa.FA_ERR_ARG   # workspace aliases o
+
+
+# --------------------------------------------------------------------------
+# packed variable-length calls
+# --------------------------------------------------------------------------
+def vfwd_args(**kw):
+    q, k, v, o, lse, cq, ck = ptrs(7)
+    args = dict(q=q, k=k, v=v, o=o, lse=lse, cu_seqlens_q=cq, cu_seqlens_k=ck, B=2, H=4, Hkv=2,
+                max_seqlen_q=100, max_seqlen_k=120, total_q=150, total_k=200, d=64, scale=0.125,
+                mask_kind=fa.MASK_CAUSAL, dtype=fa.DTYPE_BF16, stream=None)
+    args.update(kw)
+    return args
+
+
+def vbwd_args(**kw):
+    q, k, v, o, lse, do, dq, dk, dv, cq, ck, ws = ptrs(12)
+    args = dict(q=q, k=k, v=v, o=o, lse=lse, dO=do, dq=dq, dk=dk, dv=dv, cu_seqlens_q=cq, cu_seqlens_k=ck,
+                B=2, H=4, Hkv=2, max_seqlen_q=100, max_seqlen_k=120, total_q=150, total_k=200, d=64,
+                scale=0.125, mask_kind=fa.MASK_NONE, dtype=fa.DTYPE_BF16, workspace=ws,
+                workspace_bytes=fa.fa_bwd_varlen_workspace_bytes(150, 4, 64), stream=None)
+    args.update(kw)
+    return args
+
+
+def test_varlen_workspace_bytes():
+    assert fa.fa_bwd_varlen_workspace_bytes(150, 4, 64) == 2560
+    assert fa.fa_bwd_varlen_workspace_bytes(1, 1, 128) == 256
+    for bad in ((0, 1, 64), (1, 0, 64), (5, 2, 32)):
+        assert fa.fa_bwd_varlen_workspace_bytes(*bad) == 0
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse", "cu_seqlens_q", "cu_seqlens_k"])
+def test_varlen_fwd_null(name):
+    assert fa.fa_fwd_varlen(**vfwd_args(**{name: None})) == fa.FA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=0), fa.FA_ERR_SHAPE), (dict(Hkv=0), fa.FA_ERR_SHAPE),
+    (dict(H=6, Hkv=4), fa.FA_ERR_SHAPE), (dict(H=1 << 17, Hkv=1), fa.FA_ERR_SHAPE),
+    (dict(max_seqlen_q=0), fa.FA_ERR_SHAPE), (dict(max_seqlen_k=0), fa.FA_ERR_SHAPE),
+    (dict(total_q=0), fa.FA_ERR_SHAPE), (dict(total_k=-3), fa.FA_ERR_SHAPE),
+    (dict(total_q=1 << 30, H=1 << 12, Hkv=1), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(dtype=fa.DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask_kind=fa.MASK_BLOCK_SPARSE), fa.FA_ERR_MASK), (dict(mask_kind=7), fa.FA_ERR_MASK),
+    (dict(scale=math.nan), fa.FA_ERR_ARG),
+    (dict(q=A + 4), fa.FA_ERR_ALIGN), (dict(cu_seqlens_k=6 * BIG + A + 2), fa.FA_ERR_ALIGN),
+    (dict(o=A + 2 * BIG), fa.FA_ERR_ARG),            # o aliases v
+    (dict(lse=5 * BIG + A), fa.FA_ERR_ARG),          # lse aliases cu_seqlens_q
+])
+def test_varlen_fwd_validation(kw, code):
+    assert fa.fa_fwd_varlen(**vfwd_args(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dv=None), fa.FA_ERR_NULL), (dict(cu_seqlens_q=None), fa.FA_ERR_NULL),
+    (dict(H=3, Hkv=2), fa.FA_ERR_SHAPE), (dict(dtype=fa.DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask_kind=fa.MASK_BLOCK_SPARSE), fa.FA_ERR_MASK),
+    (dict(workspace=None), fa.FA_ERR_WORKSPACE), (dict(workspace_bytes=100), fa.FA_ERR_WORKSPACE),
+    (dict(dk=7 * BIG + A + 8), fa.FA_ERR_ALIGN), (dict(workspace=11 * BIG + A + 4), fa.FA_ERR_ALIGN),
+    (dict(dq=A), fa.FA_ERR_ARG),                     # dq aliases q
+    (dict(dv=7 * BIG + A), fa.FA_ERR_ARG),           # dv aliases dk
+    (dict(workspace=9 * BIG + A), fa.FA_ERR_ARG),    # workspace aliases cu_seqlens_q
+])
+def test_varlen_bwd_validation(kw, code):
+    assert fa.fa_bwd_varlen(**vbwd_args(**kw)) == code
+
+
+def test_varlen_torch_wrappers_reject_bad_tensors():
+    import torch
+    q = torch.zeros(8, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fa.forward_varlen(q, q, q, cu, cu, 8, 8)          # CPU tensors
+    with pytest.raises(ValueError):
+        fa.forward_varlen(q[None], q, q, cu, cu, 8, 8)    # wrong rank
