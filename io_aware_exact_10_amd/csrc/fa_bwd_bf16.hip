@@ -124,9 +124,8 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   }
   MaskScan ms;
   if (MASK == 2) ms.init(p.block_mask + kt, p.nblk, p.nblk);   // column kt of the mask
-  // The loop runs over (query head j, query tile it) pairs, coded as
-  // j * nqt + it; code nend means done.
-  const int nend = G * nqt;
+  // The loop runs over the visible query tiles `it` of query head j = 0, then
+  // those of head 1, ... (the visible tiles are the same in every head).
   auto next_in_head = [&](int it) -> int {
     if (MASK != 2 || it >= nqt) return it < nqt ? it : nqt;
     const int blk = it / QPB;
@@ -135,19 +134,9 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     const int t = nb == blk ? it : nb * QPB;
     return t < nqt ? t : nqt;
   };
-  auto next_tile = [&](int code) -> int {
-    int j = code / nqt, it = code - j * nqt;
-    if (j >= G) return nend;
-    it = next_in_head(it < qbeg ? qbeg : it);
-    if (it < nqt) return j * nqt + it;
-    // the visible query tiles are the same in every head
-    it = next_in_head(qbeg);
-    return it < nqt && j + 1 < G ? (j + 1) * nqt + it : nend;
-  };
   TileLoader<D, kDkvBQ, 4> ld;
   ld.init(w, lane, (int)(p.q_rs * 2));
-  auto issue = [&](int code, int buf) {
-    const int j = code / nqt, it = code - j * nqt;
+  auto issue = [&](int it, int j, int buf) {
     const int q0 = it * kDkvBQ;
     ld.load(sm.q[buf], Qg + j * p.q_hs, q0, Nq);
     ld.load(sm.dO[buf], dOg + j * p.q_hs, q0, Nq);
@@ -159,8 +148,8 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     }
   };
 
-  int it = nqt > 0 ? next_tile(0) : nend;
-  if (it < nend) issue(it, 0);
+  int it = next_in_head(qbeg), j = 0;
+  if (it < nqt) issue(it, j, 0);
 
   u32x4 kf[D / 16], vf[D / 16];
 #pragma unroll
@@ -278,8 +267,8 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
       }
     }
   };
-  auto compute = [&](int buf, int code) {
-    const int q0 = (code % nqt) * kDkvBQ;
+  auto compute = [&](int buf, int it) {
+    const int q0 = it * kDkvBQ;
     const bool needm = (MASK == 1 && q0 + off < kw0 + 31) || q0 + kDkvBQ > Nq;
     if (needm)
       tile(buf, q0, std::true_type{});
@@ -290,14 +279,19 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   wait_vmem();
   __syncthreads();
   int buf = 0;
-  while (it < nend) {
-    const int itn = next_tile(it + 1);
-    if (itn < nend) issue(itn, buf ^ 1);
+  while (it < nqt) {
+    int itn = next_in_head(it + 1), jn = j;
+    if (itn >= nqt && j + 1 < G) {   // on to the next query head of the group
+      itn = next_in_head(qbeg);
+      jn = j + 1;
+    }
+    if (itn < nqt) issue(itn, jn, buf ^ 1);
     compute(buf, it);
     wait_vmem();
     __syncthreads();
     buf ^= 1;
     it = itn;
+    j = jn;
   }
 
   if (kj < Nk) {
