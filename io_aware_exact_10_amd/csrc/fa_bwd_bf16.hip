@@ -96,10 +96,10 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
   const uint32_t L = xcd_remap(blockIdx.x, total);
-  const uint32_t bh = L / nkt;                 // (batch, K/V head)
+  const uint32_t bh = L / nkt;                 // (K/V head, batch), head-major as in the forward kernel
   const int kt = (int)(L - bh * nkt);
   const int k0 = kt * kDkvBK;
-  const int bat = (int)bh / p.Hkv, hk = (int)bh - bat * p.Hkv;
+  const int hk = (int)bh / p.B, bat = (int)bh - hk * p.B;
   const SeqView sq = seq_view(p, bat);
   if (k0 >= sq.nk) return;                     // past this sequence's keys (packed batches)
   const int Nq = sq.nq, Nk = sq.nk;
@@ -343,7 +343,7 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   uint32_t qt = L - bh * nqt;
   if (MASK == 1) qt = nqt - 1 - qt;
   const int q0 = (int)qt * kDqBQ;
-  const int bat = (int)bh / p.H, hq = (int)bh - bat * p.H;
+  const int hq = (int)bh / p.B, bat = (int)bh - hq * p.B;   // head-major, as in the forward kernel
   const SeqView sq = seq_view(p, bat);
   if (q0 >= sq.nq) return;                     // past this sequence's queries (packed batches)
   const int Nq = sq.nq, Nk = sq.nk;

@@ -78,7 +78,10 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   uint32_t qt = L - bh * nqt;
   if (MASK == 1) qt = nqt - 1 - qt;            // causal: longest rows first
   const int q0 = (int)qt * kFwdBR;
-  const int bat = (int)bh / p.H, hq = (int)bh - bat * p.H;
+  // Head-major: each XCD's contiguous share of the grid covers whole heads
+  // of every sequence, so ragged packed batches spread evenly over the XCDs
+  // and the query heads of one K/V group share an L2.
+  const int hq = (int)bh / p.B, bat = (int)bh - hq * p.B;
   const SeqView sq = seq_view(p, bat);
   if (q0 >= sq.nq) return;                     // past this sequence's queries (packed batches)
   const int Nq = sq.nq, Nk = sq.nk;

@@ -209,3 +209,33 @@ def length_mix(B: int, max_len: int, seed: int, min_len: int = 1) -> list:
     lens = rng.integers(min_len, max_len + 1, size=B).tolist()
     lens[int(rng.integers(0, B))] = max_len
     return lens
+
+
+@dataclasses.dataclass(frozen=True)
+class PackedWorkload:
+    """A packed variable-length workload: B sequences whose query and key
+    lengths are drawn by ``length_mix`` (equal per sequence), H query heads
+    sharing Hkv K/V heads."""
+    name: str
+    B: int
+    max_len: int
+    H: int
+    Hkv: int
+    d: int
+    mask_kind: int
+    backward: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def lengths(self) -> list:
+        return length_mix(self.B, self.max_len, self.seed, min_len=self.max_len // 8)
+
+
+PACKED_WORKLOADS = {
+    # 16 causal sequences of 512..4096 tokens packed back to back, 32 query
+    # heads over 8 K/V heads (grouped-query attention), d = 128.
+    "varlen_gqa": PackedWorkload("varlen_gqa", 16, 4096, 32, 8, 128, MASK_CAUSAL, True, 6),
+}

@@ -48,3 +48,40 @@ def test_workload_sampled_heads(name):
                                               w.scale, w.mask_kind, inp.mask)
             for n, got, ref in (("dq", dq, gq), ("dk", dk, gk), ("dv", dv, gv)):
                 check_grad(got[b, h].float().cpu().numpy(), ref, w.dtype, f"{name} head ({b},{h}) {n}")
+
+
+def test_packed_workload_sampled_sequences():
+    """The packed grouped-query workload at full size (16 causal sequences of
+    up to 4096 tokens, 32 query heads over 8 K/V heads, d = 128): forward and
+    backward of the whole batch on the GPU; the oracle recomputes sampled
+    sequences, and for dK/dV every query head of one K/V group."""
+    w = synth.PACKED_WORKLOADS["varlen_gqa"]
+    lens = w.lengths()
+    p = synth.packed_inputs(lens, lens, w.H, w.Hkv, w.d, w.seed)
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, do = dev(p.q_bits), dev(p.k_bits), dev(p.v_bits), dev(p.do_bits)
+    cu = torch.from_numpy(p.cu_q).cuda()
+    mx = max(lens)
+    announce(f"fa_fwd_varlen full workload {w.name} tokens {q.shape[0]} H{w.H}/{w.Hkv} d{w.d}")
+    o, lse = fa.forward_varlen(q, k, v, cu, cu, mx, mx, w.scale, w.mask_kind)
+    announce(f"fa_bwd_varlen full workload {w.name}")
+    dq, dk, dv = fa.backward_varlen(q, k, v, o, lse, do, cu, cu, mx, mx, w.scale, w.mask_kind)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    G = w.H // w.Hkv
+    hk = 1
+    for b in (6, int(np.argmax(lens))):
+        a, e = int(p.cu_q[b]), int(p.cu_q[b + 1])
+        ref_dk = np.zeros((e - a, w.d))
+        ref_dv = np.zeros((e - a, w.d))
+        for h in range(hk * G, (hk + 1) * G):
+            args = (p.q[a:e, h], p.k[a:e, hk], p.v[a:e, hk])
+            O, L = oracle.forward_head(*args, w.scale, w.mask_kind)
+            check_forward(o[a:e, h].float().cpu().numpy(), lse[h, a:e].cpu().numpy(), O, L, synth.DTYPE_BF16,
+                          f"{w.name} seq {b} head {h}")
+            gq, gk, gv = oracle.backward_head(*args, p.do[a:e, h], w.scale, w.mask_kind)
+            check_grad(dq[a:e, h].float().cpu().numpy(), gq, synth.DTYPE_BF16, f"{w.name} seq {b} head {h} dq")
+            ref_dk += gk
+            ref_dv += gv
+        check_grad(dk[a:e, hk].float().cpu().numpy(), ref_dk, synth.DTYPE_BF16, f"{w.name} seq {b} kv head {hk} dk")
+        check_grad(dv[a:e, hk].float().cpu().numpy(), ref_dv, synth.DTYPE_BF16, f"{w.name} seq {b} kv head {hk} dv")
