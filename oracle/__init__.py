@@ -14,11 +14,13 @@ from .attention import (  # noqa: F401
     backward_head,
     backward_varlen,
     causal_offset,
+    combine_partials,
     forward,
     forward_head,
     forward_varlen,
     online_forward_head,
     online_softmax_row,
+    partial_head,
     probabilities_head,
     row_term_head,
     visible,

@@ -272,6 +272,55 @@ def backward_varlen(q, k, v, do, cu_q, cu_k, scale, mask_kind=MASK_NONE):
 
 
 # ----------------------------------------------------------------------------
+# split keys: partial results over key ranges, then the combine rule
+# ----------------------------------------------------------------------------
+def partial_head(q, k, v, scale, keys, mask_kind=MASK_NONE, offset=None):
+    """(O_s, LSE_s) of one head over the key indices ``keys`` only: the
+    definition restricted to that range (visibility is still decided by the
+    key's position in the whole sequence). A row that sees none of these keys
+    gets O_s = 0, LSE_s = -inf."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    keys = np.asarray(keys, dtype=np.int64)
+    Nq, Nk = q.shape[0], k.shape[0]
+    offset = causal_offset(Nq, Nk) if offset is None else offset
+    s = scale * (q @ k[keys].T)
+    vis = visible(np.arange(Nq), Nk, mask_kind, offset=offset)[:, keys]
+    s[~vis] = -np.inf
+    live = vis.any(axis=1)
+    m = np.where(live, s.max(axis=1) if keys.size else 0.0, 0.0)
+    e = np.exp(s - m[:, None])
+    den = np.where(live, e.sum(axis=1), 1.0)
+    o = (e / den[:, None]) @ v[keys]
+    with np.errstate(divide="ignore"):
+        lse = np.where(live, m + np.log(den), -np.inf)
+    return o, lse
+
+
+def combine_partials(o_parts, lse_parts):
+    """Merge per-key-range results of the same rows into the full result.
+
+    The block-combine rule ([T] "Mathematical Correctness": the exponential
+    sum of a row is the sum over blocks of each block's sum times
+    exp(block max - overall max); [C] "Core ideas": one log-sum-exp per
+    row): LSE = max_s LSE_s + ln sum_s exp(LSE_s - max_s LSE_s) and
+    O = sum_s exp(LSE_s - LSE) O_s. Ranges a row does not see (LSE_s = -inf)
+    weigh 0; a row that sees nothing gets O = 0, LSE = -inf.
+    """
+    o_parts = [_f64(o) for o in o_parts]
+    L = np.stack([_f64(x) for x in lse_parts])           # [S, rows]
+    m = L.max(axis=0)
+    live = np.isfinite(m)
+    ms = np.where(live, m, 0.0)
+    w = np.exp(L - ms[None, :])                            # exp(-inf) = 0
+    tot = w.sum(axis=0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(live, ms + np.log(np.where(live, tot, 1.0)), -np.inf)
+    wn = w / np.where(live, tot, 1.0)[None, :]
+    o = sum(wn[s][:, None] * o_parts[s] for s in range(len(o_parts)))
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
 # the pages' blockwise online algorithm (float64), used only to pin the above
 # ----------------------------------------------------------------------------
 def online_softmax_row(x, values, block_sizes):

@@ -440,3 +440,49 @@ def test_varlen_single_sequence_equals_dense_heads():
     for h in range(H):
         Oh, Lh = oracle.forward_head(q[:, h], k[:, h], v[:, h], sc, MASK_CAUSAL)
         assert np.array_equal(O[:, h], Oh) and np.array_equal(L[h], Lh)
+
+
+# --------------------------------------------------------------------------
+# key ranges computed apart and merged with the block-combine rule
+# ([T] "Mathematical Correctness"; [C] "Core ideas")
+# --------------------------------------------------------------------------
+def test_combine_two_single_key_ranges_closed_form():
+    """One query, keys with scores a and b in two ranges: the merged LSE is
+    ln(e^a + e^b) and O the softmax-weighted mix of the two values."""
+    a, b = 0.3, -1.7
+    o, lse = oracle.combine_partials([np.array([[2.0]]), np.array([[-5.0]])], [np.array([a]), np.array([b])])
+    assert abs(lse[0] - math.log(math.exp(a) + math.exp(b))) < 1e-15
+    wa = math.exp(a) / (math.exp(a) + math.exp(b))
+    assert abs(o[0, 0] - (wa * 2.0 + (1 - wa) * -5.0)) < 1e-15
+
+
+@pytest.mark.parametrize("mask_kind", [MASK_NONE, MASK_CAUSAL])
+def test_split_key_ranges_combine_to_the_definition(mask_kind):
+    rng = np.random.default_rng(301)
+    for nq, nk in ((1, 200), (5, 97), (16, 300), (20, 12)):
+        d = 7
+        q, k, v = rnd(302, nq, d), rnd(303, nk, d), rnd(304, nk, d)
+        O, L = oracle.forward_head(q, k, v, 0.6, mask_kind)
+        for _ in range(4):
+            cuts = np.sort(rng.choice(np.arange(1, nk), size=int(rng.integers(0, min(9, nk - 1))), replace=False))
+            bounds = np.concatenate([[0], cuts, [nk]]).astype(int)
+            parts = [oracle.partial_head(q, k, v, 0.6, np.arange(bounds[i], bounds[i + 1]), mask_kind)
+                     for i in range(len(bounds) - 1)]
+            o, lse = oracle.combine_partials([x[0] for x in parts], [x[1] for x in parts])
+            assert np.allclose(o, O, rtol=0, atol=1e-13)
+            fin = np.isfinite(L)
+            assert (np.isfinite(lse) == fin).all() and np.allclose(lse[fin], L[fin], rtol=0, atol=1e-13)
+
+
+def test_combine_with_empty_ranges():
+    """A range no row sees weighs nothing; all ranges empty -> O = 0, LSE = -inf."""
+    nq, nk, d = 3, 40, 4
+    q, k, v = rnd(311, nq, d), rnd(312, nk, d), rnd(313, nk, d)
+    O, L = oracle.forward_head(q, k, v, 0.9, MASK_NONE)
+    full = oracle.partial_head(q, k, v, 0.9, np.arange(nk))
+    empty = oracle.partial_head(q, k, v, 0.9, np.arange(0))
+    assert (empty[0] == 0).all() and np.isneginf(empty[1]).all()
+    o, lse = oracle.combine_partials([empty[0], full[0], empty[0]], [empty[1], full[1], empty[1]])
+    assert np.allclose(o, O, atol=1e-14) and np.allclose(lse, L, atol=1e-14)
+    o, lse = oracle.combine_partials([empty[0]] * 2, [empty[1]] * 2)
+    assert (o == 0).all() and np.isneginf(lse).all()
