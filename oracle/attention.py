@@ -48,7 +48,8 @@ unequal lengths; the offset above (queries are the last Nq positions of the
 key sequence) is the reading taken.
 
 A query row with no visible key has O = 0, LSE = -inf and contributes no
-gradient (it cannot occur for causal or unmasked attention).
+gradient (a user block mask can produce one; so can causal attention with
+more queries than keys, and a sequence without keys).
 
 Besides the definition, the module holds the pages' blockwise online
 algorithm in float64 (``online_forward_head``, ``online_softmax_row``): it
@@ -128,7 +129,7 @@ def forward_head(q, k, v, scale, mask_kind=MASK_NONE, block_mask=None, rows=None
         r = rows[c0:c0 + chunk]
         s, vis = _scores(q[r], k, scale, r, N, mask_kind, block_mask, block, offset)
         live = vis.any(axis=1)
-        m = np.where(live, s.max(axis=1), 0.0)
+        m = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
         e = np.exp(s - m[:, None])                 # exp(-inf) = 0 on masked keys
         den = e.sum(axis=1)
         with np.errstate(divide="ignore"):
@@ -147,7 +148,7 @@ def probabilities_head(q, k, scale, mask_kind=MASK_NONE, block_mask=None, rows=N
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     s, vis = _scores(q[rows], k, scale, rows, N, mask_kind, block_mask, block, offset)
     live = vis.any(axis=1)
-    m = np.where(live, s.max(axis=1), 0.0)
+    m = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
     e = np.exp(s - m[:, None])
     den = np.where(live, e.sum(axis=1), 1.0)
     return e / den[:, None]
@@ -172,7 +173,7 @@ def backward_head(q, k, v, do, scale, mask_kind=MASK_NONE, block_mask=None,
         r = np.arange(c0, min(Nq, c0 + chunk))
         s, vis = _scores(q[r], k, scale, r, Nk, mask_kind, block_mask, block, offset)
         live = vis.any(axis=1)
-        m = np.where(live, s.max(axis=1), 0.0)
+        m = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
         e = np.exp(s - m[:, None])
         p = e / np.where(live, e.sum(axis=1), 1.0)[:, None]
         doc = do[r]
@@ -287,7 +288,7 @@ def partial_head(q, k, v, scale, keys, mask_kind=MASK_NONE, offset=None):
     vis = visible(np.arange(Nq), Nk, mask_kind, offset=offset)[:, keys]
     s[~vis] = -np.inf
     live = vis.any(axis=1)
-    m = np.where(live, s.max(axis=1) if keys.size else 0.0, 0.0)
+    m = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
     e = np.exp(s - m[:, None])
     den = np.where(live, e.sum(axis=1), 1.0)
     o = (e / den[:, None]) @ v[keys]

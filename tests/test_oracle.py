@@ -486,3 +486,17 @@ def test_combine_with_empty_ranges():
     assert np.allclose(o, O, atol=1e-14) and np.allclose(lse, L, atol=1e-14)
     o, lse = oracle.combine_partials([empty[0]] * 2, [empty[1]] * 2)
     assert (o == 0).all() and np.isneginf(lse).all()
+
+
+def test_no_keys_at_all():
+    """Zero keys: every row is empty (O = 0, LSE = -inf, no gradient), the
+    same convention as a fully masked row."""
+    q, do = rnd(321, 3, 4), rnd(322, 3, 4)
+    k = v = np.zeros((0, 4))
+    for mk in (MASK_NONE, MASK_CAUSAL):
+        O, L = oracle.forward_head(q, k, v, 0.5, mk)
+        assert O.shape == (3, 4) and (O == 0).all() and np.isneginf(L).all()
+        dq, dk, dv = oracle.backward_head(q, k, v, do, 0.5, mk)
+        assert (dq == 0).all() and dk.shape == (0, 4) and dv.shape == (0, 4)
+    O, L = oracle.forward_varlen(rnd(323, 2, 2, 4), np.zeros((0, 1, 4)), np.zeros((0, 1, 4)), [0, 2], [0, 0], 0.5)
+    assert (O == 0).all() and np.isneginf(L).all()
