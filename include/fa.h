@@ -198,6 +198,41 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
                   int total_q, int total_k, int d, float scale, int mask_kind, int dtype,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Split-key forward for packed batches with few queries per sequence against
+ * long key sequences (decoding). Computes exactly what fa_fwd_varlen computes
+ * (same layouts, heads, masks, outputs and untouched rows), organised for
+ * this shape: one workgroup per (K/V head, sequence, key range) stacks the
+ * queries of all H / Hkv query heads that read the K/V head, so each K/V tile
+ * is read once per group, and the key range of every sequence is split over
+ * `splits` workgroups. Each range's partial result is normalised over that
+ * range and merged afterwards with the block-combine rule of "Flash
+ * Attention — Revolutionizing Transformer Efficiency Through Memory-Aware
+ * Algorithms", "Mathematical Correctness" (a row's exponential sum is the
+ * sum of the blocks' sums, each scaled by exp(block max - overall max)):
+ *   LSE = max_s LSE_s + ln sum_s exp(LSE_s - max_s LSE_s),
+ *   O = sum_s exp(LSE_s - LSE) O_s.
+ * Rounding differs from fa_fwd_varlen (fp32 partials are merged before the
+ * single rounding of O to bf16).
+ *
+ * Limits. (H / Hkv) * max_seqlen_q <= 128, else FA_ERR_UNSUPPORTED; the other
+ *   limits and status codes are those of fa_fwd_varlen.
+ * Splits. num_splits = 0 lets the library choose; 1..128 forces a count;
+ *   anything else is FA_ERR_ARG. fa_splitkv_splits returns the count a call
+ *   with these arguments uses (or a negative status).
+ * Workspace. Caller-owned device memory, 16-byte aligned, of at least
+ *   fa_splitkv_workspace_bytes(total_q, H, d, splits) bytes (fp32 partial O
+ *   and LSE of every range); contents ignored on entry, unspecified on exit.
+ *   Two calls in flight at once need separate workspaces.
+ */
+int fa_splitkv_splits(int B, int Hkv, int max_seqlen_k, int num_splits);
+size_t fa_splitkv_workspace_bytes(int total_q, int H, int d, int splits);
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int* cu_seqlens_q, const int* cu_seqlens_k,
+                   int B, int H, int Hkv, int max_seqlen_q, int max_seqlen_k,
+                   int total_q, int total_k, int d, float scale, int mask_kind, int dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a fa_status value ("unknown status" otherwise). */
 const char* fa_status_string(int status);
 

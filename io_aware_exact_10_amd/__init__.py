@@ -30,8 +30,8 @@ __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_BLOCK_SPARSE", "DTYPE_BF16", "DTYPE_F32",
     "FAError", "fa_fwd", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen", "fa_bwd_varlen",
-    "fa_bwd_varlen_workspace_bytes",
-    "forward", "backward", "forward_varlen", "backward_varlen", "library_path", "lib",
+    "fa_bwd_varlen_workspace_bytes", "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
+    "forward", "backward", "forward_varlen", "backward_varlen", "forward_splitkv", "library_path", "lib",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +87,12 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_varlen.restype = i
         L.fa_bwd_varlen_workspace_bytes.argtypes = [i, i, i]
         L.fa_bwd_varlen_workspace_bytes.restype = sz
+        L.fa_splitkv_splits.argtypes = [i, i, i, i]
+        L.fa_splitkv_splits.restype = i
+        L.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i]
+        L.fa_splitkv_workspace_bytes.restype = sz
+        L.fa_fwd_splitkv.argtypes = [vp] * 7 + [i] * 8 + [f, i, i, i, vp, sz, vp]
+        L.fa_fwd_splitkv.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -155,6 +161,22 @@ def fa_bwd_varlen(q, k, v, o, lse, dO, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B
     return int(lib().fa_bwd_varlen(q, k, v, o, lse, dO, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, H, Hkv,
                                    max_seqlen_q, max_seqlen_k, total_q, total_k, d, ctypes.c_float(scale),
                                    mask_kind, dtype, workspace, workspace_bytes, stream))
+
+
+def fa_splitkv_splits(B: int, Hkv: int, max_seqlen_k: int, num_splits: int) -> int:
+    return int(lib().fa_splitkv_splits(B, Hkv, max_seqlen_k, num_splits))
+
+
+def fa_splitkv_workspace_bytes(total_q: int, H: int, d: int, splits: int) -> int:
+    return int(lib().fa_splitkv_workspace_bytes(total_q, H, d, splits))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, Hkv, max_seqlen_q, max_seqlen_k,
+                   total_q, total_k, d, scale, mask_kind, dtype, num_splits, workspace, workspace_bytes,
+                   stream) -> int:
+    return int(lib().fa_fwd_splitkv(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, Hkv, max_seqlen_q,
+                                    max_seqlen_k, total_q, total_k, d, ctypes.c_float(scale), mask_kind, dtype,
+                                    num_splits, workspace, workspace_bytes, stream))
 
 
 # ---------------------------------------------------------------------------
@@ -324,3 +346,29 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     if st != FA_OK:
         raise FAError(st, "fa_bwd_varlen")
     return dq, dk, dv
+
+
+def forward_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None,
+                    mask_kind=MASK_NONE, num_splits=0, out=None, lse=None, workspace=None):
+    """Split-key packed-batch forward (few queries per sequence, long keys);
+    same arguments and results as ``forward_varlen``. ``num_splits`` = 0 lets
+    the library choose the number of key ranges per sequence."""
+    _check_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    Tq, H, d = q.shape
+    Tk, Hkv = k.shape[:2]
+    B = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    splits = fa_splitkv_splits(B, Hkv, int(max_seqlen_k), int(num_splits))
+    if splits < 0:
+        raise FAError(splits, "fa_splitkv_splits")
+    if workspace is None:
+        workspace = torch.empty(fa_splitkv_workspace_bytes(Tq, H, d, splits), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Hkv, int(max_seqlen_q),
+                        int(max_seqlen_k), Tq, Tk, d, scale, mask_kind, DTYPE_BF16, int(num_splits),
+                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_splitkv")
+    return o, lse

@@ -362,3 +362,86 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// split-key forward of packed batches with few queries per sequence (bf16)
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kMaxSplits = 128;
+constexpr int kMaxSplitRows = 128;   // (H / Hkv) * max_seqlen_q: query rows of one workgroup
+
+size_t splitkv_o_bytes(int total_q, int H, int d, int splits) {
+  return ((size_t)splits * (size_t)total_q * (size_t)H * (size_t)d * sizeof(float) + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_splitkv_splits(int B, int Hkv, int max_seqlen_k, int num_splits) {
+  if (B < 1 || Hkv < 1 || max_seqlen_k < 1) return FA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  if (num_splits > 0) return num_splits;
+  // Every range has the same number of keys, sized from the longest
+  // sequence (shorter sequences use fewer ranges): about 8192 ranges if every
+  // sequence were that long (some 32 per compute unit, so the ragged last
+  // ranges even out), and at least 256 keys per range where there are keys
+  // enough.
+  const int64_t groups = (int64_t)B * Hkv;
+  int64_t s = (8192 + groups - 1) / groups;
+  const int64_t cap = ((int64_t)max_seqlen_k + 255) / 256;
+  if (s > cap) s = cap;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
+size_t fa_splitkv_workspace_bytes(int total_q, int H, int d, int splits) {
+  if (total_q < 1 || H < 1 || (d != 64 && d != 128) || splits < 1 || splits > kMaxSplits) return 0;
+  const size_t lse = ((size_t)splits * (size_t)H * (size_t)total_q * sizeof(float) + 255) & ~(size_t)255;
+  return splitkv_o_bytes(total_q, H, d, splits) + lse;
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int* cu_seqlens_q, const int* cu_seqlens_k,
+                   int B, int H, int Hkv, int max_seqlen_q, int max_seqlen_k,
+                   int total_q, int total_k, int d, float scale, int mask_kind, int dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  int st = varlen_check(B, H, Hkv, max_seqlen_q, max_seqlen_k, total_q, total_k, d, scale, mask_kind, dtype);
+  if (st != FA_OK) return st;
+  if ((int64_t)(H / Hkv) * max_seqlen_q > kMaxSplitRows) return FA_ERR_UNSUPPORTED;
+  const int splits = fa_splitkv_splits(B, Hkv, max_seqlen_k, num_splits);
+  if (splits < 0) return splits;
+  if ((int64_t)B * Hkv * splits >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  const size_t need = fa_splitkv_workspace_bytes(total_q, H, d, splits);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
+  const size_t qb = (size_t)total_q * H * d * 2, kb = (size_t)total_k * Hkv * d * 2;
+  const size_t lb = (size_t)total_q * H * sizeof(float), cb = (size_t)(B + 1) * sizeof(int);
+  const void* ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
+  const size_t insz[5] = {qb, kb, kb, cb, cb};
+  const void* outs[3] = {o, lse, workspace};
+  const size_t outsz[3] = {qb, lb, need};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ARG;
+  }
+  fa::AttnParams p = varlen_params(cu_seqlens_q, cu_seqlens_k, B, H, Hkv, max_seqlen_q, max_seqlen_k, total_q,
+                                   total_k, d, scale);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.splits = splits;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((uint8_t*)workspace + splitkv_o_bytes(total_q, H, d, splits));
+  return fa::launch_splitkv_bf16(p, mask_kind, stream) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -148,6 +148,12 @@ struct TileLoader {
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Cheap fragment addressing for swizzled tiles. The swizzle only XORs the
 // chunk field (bits 4..7 of the byte offset within a 2D-byte row), so for

@@ -41,6 +41,11 @@ struct AttnParams {
   // goes to entry (r % rt_inner) * rt_hs + r / rt_inner of the row term
   // (dense: rt_inner = 1, the identity; packed: r = token * H + head).
   int64_t rt_rows, rt_inner, rt_hs;
+  // Split-key forward: key ranges per sequence and the per-range partial
+  // results (fp32 O [splits, Tq, H, d], LSE [splits, H, Tq]; workspace).
+  int splits;
+  float* part_o;
+  float* part_lse;
 };
 
 // Per-sequence view used by the kernels: lengths and the element offsets of
@@ -85,6 +90,8 @@ enum BwdStep { kBwdRowterm = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7 };
 int launch_fwd_bf16(const AttnParams& p, int mask_kind, hipStream_t stream);
 int launch_bwd_bf16(const AttnParams& p, int mask_kind, int steps, hipStream_t stream);
 int launch_fwd_f32(const AttnParams& p, int mask_kind, hipStream_t stream);
+// Split-key forward of a packed batch (partial ranges, then the merge).
+int launch_splitkv_bf16(const AttnParams& p, int mask_kind, hipStream_t stream);
 int launch_bwd_f32(const AttnParams& p, int mask_kind, int steps, hipStream_t stream);
 
 }  // namespace fa

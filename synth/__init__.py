@@ -213,9 +213,10 @@ def length_mix(B: int, max_len: int, seed: int, min_len: int = 1) -> list:
 
 @dataclasses.dataclass(frozen=True)
 class PackedWorkload:
-    """A packed variable-length workload: B sequences whose query and key
-    lengths are drawn by ``length_mix`` (equal per sequence), H query heads
-    sharing Hkv K/V heads."""
+    """A packed variable-length workload: B sequences whose key lengths are
+    drawn by ``length_mix``, H query heads sharing Hkv K/V heads. Query
+    lengths equal the key lengths, or are ``queries`` per sequence when that
+    is set (decoding: a few new tokens against a long cache)."""
     name: str
     B: int
     max_len: int
@@ -225,6 +226,7 @@ class PackedWorkload:
     mask_kind: int
     backward: bool
     seed: int
+    queries: int = 0
 
     @property
     def scale(self) -> float:
@@ -233,9 +235,15 @@ class PackedWorkload:
     def lengths(self) -> list:
         return length_mix(self.B, self.max_len, self.seed, min_len=self.max_len // 8)
 
+    def query_lengths(self) -> list:
+        return [self.queries] * self.B if self.queries else self.lengths()
+
 
 PACKED_WORKLOADS = {
     # 16 causal sequences of 512..4096 tokens packed back to back, 32 query
     # heads over 8 K/V heads (grouped-query attention), d = 128.
     "varlen_gqa": PackedWorkload("varlen_gqa", 16, 4096, 32, 8, 128, MASK_CAUSAL, True, 6),
+    # decoding: one new query per sequence against 64 cached sequences of
+    # 1024..8192 keys, 32 query heads over 8 K/V heads, d = 128.
+    "decode_splitkv": PackedWorkload("decode_splitkv", 64, 8192, 32, 8, 128, MASK_CAUSAL, False, 7, queries=1),
 }

@@ -48,7 +48,8 @@ def test_library_exports_every_declared_symbol():
     names = fa.declared_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen",
-                          "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes"}
+                          "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_splitkv_splits",
+                          "fa_splitkv_workspace_bytes", "fa_fwd_splitkv"}
     L = fa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -257,3 +258,46 @@ def test_varlen_torch_wrappers_reject_bad_tensors():
         fa.forward_varlen(q, q, q, cu, cu, 8, 8)          # CPU tensors
     with pytest.raises(ValueError):
         fa.forward_varlen(q[None], q, q, cu, cu, 8, 8)    # wrong rank
+
+
+# --------------------------------------------------------------------------
+# split-key forward
+# --------------------------------------------------------------------------
+def skv_args(**kw):
+    q, k, v, o, lse, cq, ck, ws = ptrs(8)
+    args = dict(q=q, k=k, v=v, o=o, lse=lse, cu_seqlens_q=cq, cu_seqlens_k=ck, B=4, H=32, Hkv=8,
+                max_seqlen_q=2, max_seqlen_k=5000, total_q=8, total_k=20000, d=128, scale=0.088,
+                mask_kind=fa.MASK_CAUSAL, dtype=fa.DTYPE_BF16, num_splits=0, workspace=ws,
+                workspace_bytes=1 << 24, stream=None)
+    args.update(kw)
+    return args
+
+
+def test_splitkv_split_choice_and_workspace():
+    assert fa.fa_splitkv_splits(4, 8, 5000, 0) == 20          # ceil(5000 / 256): ranges of >= 256 keys
+    assert fa.fa_splitkv_splits(64, 8, 100000, 0) == 16       # 512 (sequence, head) groups x 16 = 8192
+    assert fa.fa_splitkv_splits(1, 1, 64, 0) == 1
+    assert fa.fa_splitkv_splits(1, 1, 1 << 20, 0) == 128      # capped
+    assert fa.fa_splitkv_splits(2, 2, 100, 7) == 7            # forced
+    assert fa.fa_splitkv_splits(2, 2, 100, 129) == fa.FA_ERR_ARG
+    assert fa.fa_splitkv_splits(2, 2, 100, -1) == fa.FA_ERR_ARG
+    assert fa.fa_splitkv_splits(0, 2, 100, 0) == fa.FA_ERR_SHAPE
+    assert fa.fa_splitkv_workspace_bytes(8, 32, 128, 20) == 20 * 8 * 32 * 128 * 4 + 20 * 32 * 8 * 4
+    assert fa.fa_splitkv_workspace_bytes(8, 32, 128, 0) == 0
+    assert fa.fa_splitkv_workspace_bytes(8, 32, 96, 1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(cu_seqlens_k=None), fa.FA_ERR_NULL),
+    (dict(H=6, Hkv=4), fa.FA_ERR_SHAPE), (dict(max_seqlen_q=0), fa.FA_ERR_SHAPE),
+    (dict(max_seqlen_q=17, H=32, Hkv=4), fa.FA_ERR_UNSUPPORTED),     # 8 x 17 > 128 stacked rows
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED), (dict(dtype=fa.DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask_kind=fa.MASK_BLOCK_SPARSE), fa.FA_ERR_MASK), (dict(scale=math.inf), fa.FA_ERR_ARG),
+    (dict(num_splits=200), fa.FA_ERR_ARG),
+    (dict(workspace=None), fa.FA_ERR_WORKSPACE), (dict(workspace_bytes=1024), fa.FA_ERR_WORKSPACE),
+    (dict(workspace=7 * BIG + A + 8), fa.FA_ERR_ALIGN), (dict(lse=4 * BIG + A + 2), fa.FA_ERR_ALIGN),
+    (dict(o=A + BIG), fa.FA_ERR_ARG),                 # o aliases k
+    (dict(workspace=5 * BIG + A), fa.FA_ERR_ARG),     # workspace aliases cu_seqlens_q
+])
+def test_splitkv_validation(kw, code):
+    assert fa.fa_fwd_splitkv(**skv_args(**kw)) == code

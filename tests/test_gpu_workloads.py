@@ -85,3 +85,28 @@ def test_packed_workload_sampled_sequences():
             ref_dv += gv
         check_grad(dk[a:e, hk].float().cpu().numpy(), ref_dk, synth.DTYPE_BF16, f"{w.name} seq {b} kv head {hk} dk")
         check_grad(dv[a:e, hk].float().cpu().numpy(), ref_dv, synth.DTYPE_BF16, f"{w.name} seq {b} kv head {hk} dv")
+
+
+def test_decode_workload_sampled_sequences():
+    """The decoding workload at full size (one query per sequence against 64
+    cached sequences of 1024..8192 keys, 32 query heads over 8 K/V heads,
+    d = 128) through the split-key forward; the oracle recomputes every head
+    of sampled sequences."""
+    w = synth.PACKED_WORKLOADS["decode_splitkv"]
+    lens, qlens = w.lengths(), w.query_lengths()
+    p = synth.packed_inputs(qlens, lens, w.H, w.Hkv, w.d, w.seed)
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(p.q_bits), dev(p.k_bits), dev(p.v_bits)
+    cq, ck = torch.from_numpy(p.cu_q).cuda(), torch.from_numpy(p.cu_k).cuda()
+    announce(f"fa_fwd_splitkv full workload {w.name} keys {k.shape[0]} H{w.H}/{w.Hkv} d{w.d}")
+    o, lse = fa.forward_splitkv(q, k, v, cq, ck, max(qlens), max(lens), w.scale, w.mask_kind)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    G = w.H // w.Hkv
+    for b in (0, int(np.argmax(lens)), int(np.argmin(lens)), w.B - 1):
+        a, e = int(p.cu_q[b]), int(p.cu_q[b + 1])
+        ka, ke = int(p.cu_k[b]), int(p.cu_k[b + 1])
+        for h in range(w.H):
+            O, L = oracle.forward_head(p.q[a:e, h], p.k[ka:ke, h // G], p.v[ka:ke, h // G], w.scale, w.mask_kind)
+            check_forward(o[a:e, h].float().cpu().numpy(), lse[h, a:e].cpu().numpy(), O, L, synth.DTYPE_BF16,
+                          f"{w.name} seq {b} head {h}")
