@@ -39,34 +39,35 @@ namespace fa {
 constexpr int kFwdBC = 64;       // keys per LDS tile
 constexpr int kMaskBlock = 128;  // block-sparse mask granularity
 
-// Waves per workgroup (32 query rows each). Eight waves share every K/V tile
-// copied into LDS among 256 queries; block-sparse keeps four so that a
+// Workgroup shape: NW waves of 32 query rows each, NBUF K/V tiles in LDS
+// (NBUF - 1 copies in flight while one tile is computed). Four waves by
+// default; from 16K queries on, eight waves (256 queries share every K/V
+// tile copied into LDS), 5 % faster at 32K. Double buffering in both: a
+// third buffer was measured slower. Block-sparse keeps four waves so a
 // workgroup's queries stay inside one 128-row mask block.
-#ifndef FA_FWD_WAVES
-#define FA_FWD_WAVES 4
-#endif
-template <int D, int MASK>
+template <int D, int MASK, int NW_, int NBUF_>
 struct FwdShape {
-  static constexpr int NW = MASK == 2 ? 4 : FA_FWD_WAVES;
+  static constexpr int NW = NW_;
+  static constexpr int NBUF = NBUF_;
   static constexpr int BR = 32 * NW;
   static constexpr int THREADS = 64 * NW;
 };
 
-template <int D>
+template <int D, int NBUF>
 struct alignas(16) FwdSmem {
-  uint8_t k[2][kFwdBC * D * 2];   // swizzled row-major K tiles
-  uint8_t v[2][kFwdBC * D * 2];   // swizzled row-major V tiles
+  uint8_t k[NBUF][kFwdBC * D * 2];   // swizzled row-major K tiles
+  uint8_t v[NBUF][kFwdBC * D * 2];   // swizzled row-major V tiles
 };
 
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
-template <int D, int MASK>
-__global__ __launch_bounds__((FwdShape<D, MASK>::THREADS))
-__attribute__((amdgpu_waves_per_eu(D == 128 || FwdShape<D, MASK>::NW == 8 ? 2 : 3)))
+template <int D, int MASK, int NW_, int NBUF>
+__global__ __launch_bounds__((FwdShape<D, MASK, NW_, NBUF>::THREADS))
+__attribute__((amdgpu_waves_per_eu(D == 128 || NW_ == 8 ? 2 : 3)))
 void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
-  __shared__ FwdSmem<D> sm;
-  constexpr int NW = FwdShape<D, MASK>::NW;
-  constexpr int kFwdBR = FwdShape<D, MASK>::BR;
+  __shared__ FwdSmem<D, NBUF> sm;
+  constexpr int NW = NW_;
+  constexpr int kFwdBR = FwdShape<D, MASK, NW_, NBUF>::BR;
   constexpr int TPB = kMaskBlock / kFwdBC;                 // key tiles per mask block
   constexpr int NDT = D / 32;                              // 32-row blocks of O^T
 
@@ -255,17 +256,41 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
       tile(buf, kt, std::false_type{});
   };
 
-  wait_vmem();
-  __syncthreads();
+  // NBUF - 1 tiles are issued ahead. At the top of an iteration tile kt is
+  // complete in buffer `buf`; the tile NBUF - 1 ahead goes into the buffer
+  // computed in the previous iteration (free after that iteration's barrier).
+  constexpr int kPerTile = 2 * TileLoader<D, kFwdBC, NW>::PER;   // this wave's copies per K+V tile
+  int ahead[NBUF > 2 ? NBUF - 2 : 1];          // tiles issued after kt, in order
+#pragma unroll
+  for (int j = 0; j + 2 < NBUF; ++j) {
+    const int prev = j == 0 ? kt : ahead[j - 1];
+    ahead[j] = prev < kend ? next_tile(prev + 1) : kend;
+    if (ahead[j] < kend) issue(ahead[j], j + 1);
+  }
+  auto wait_next = [&](int last_issued) {      // the oldest outstanding tile is complete
+    if (NBUF > 2 && last_issued < kend)
+      wait_vmem_n<(NBUF > 2 ? kPerTile * (NBUF - 2) : 0)>();
+    else
+      wait_vmem();
+    __syncthreads();
+  };
+  wait_next(NBUF > 2 ? ahead[NBUF > 2 ? NBUF - 3 : 0] : kend);
   int buf = 0;
   while (kt < kend) {
-    const int ktn = next_tile(kt + 1);
-    if (ktn < kend) issue(ktn, buf ^ 1);
+    const int last = NBUF > 2 ? ahead[NBUF > 2 ? NBUF - 3 : 0] : kt;
+    const int ktn = last < kend ? next_tile(last + 1) : kend;   // NBUF - 1 tiles after kt
+    if (ktn < kend) issue(ktn, (buf + NBUF - 1) % NBUF);
     compute(buf, kt);
-    wait_vmem();
-    __syncthreads();
-    buf ^= 1;
-    kt = ktn;
+    wait_next(ktn);
+    buf = (buf + 1) % NBUF;
+    if (NBUF > 2) {
+      kt = ahead[0];
+#pragma unroll
+      for (int j = 0; j + 3 < NBUF; ++j) ahead[j] = ahead[j + 1];
+      ahead[NBUF > 2 ? NBUF - 3 : 0] = ktn;
+    } else {
+      kt = ktn;
+    }
   }
 
   // Epilogue: combine the two lane halves' partial sums, normalise, store.
@@ -286,15 +311,30 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   }
 }
 
-template <int D, int MASK>
-static int launch_fwd_t(const AttnParams& p, hipStream_t stream) {
-  using S = FwdShape<D, MASK>;
+#ifndef FA_FWD_LONG_N
+#define FA_FWD_LONG_N 16384      // query length from which the eight-wave shape is used
+#endif
+#ifndef FA_FWD_LONG_NBUF
+#define FA_FWD_LONG_NBUF 2
+#endif
+
+template <int D, int MASK, int NW, int NBUF>
+static int launch_fwd_s(const AttnParams& p, hipStream_t stream) {
+  using S = FwdShape<D, MASK, NW, NBUF>;
   const uint32_t nqt = (uint32_t)((p.Nq + S::BR - 1) / S::BR);
   const uint32_t total = nqt * (uint32_t)p.B * (uint32_t)p.H;
   AttnParams pp = p;
   void* args[] = {&pp, (void*)&nqt, (void*)&total};
-  return (int)hipLaunchKernel((const void*)&fwd_bf16_kernel<D, MASK>, dim3(total), dim3(S::THREADS),
+  return (int)hipLaunchKernel((const void*)&fwd_bf16_kernel<D, MASK, NW, NBUF>, dim3(total), dim3(S::THREADS),
                               args, 0, stream);
+}
+
+template <int D, int MASK>
+static int launch_fwd_t(const AttnParams& p, hipStream_t stream) {
+  if constexpr (MASK != 2) {
+    if (p.Nq >= FA_FWD_LONG_N) return launch_fwd_s<D, MASK, 8, FA_FWD_LONG_NBUF>(p, stream);
+  }
+  return launch_fwd_s<D, MASK, 4, 2>(p, stream);
 }
 
 int launch_fwd_bf16(const AttnParams& p, int mask_kind, hipStream_t stream) {

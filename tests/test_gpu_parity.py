@@ -181,3 +181,20 @@ def test_backward_steps_match_fa_bwd(mask_kind, dtype):
     torch.cuda.synchronize()
     for a, b in zip(ref, (dq, dk, dv)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mask_kind", [NONE, CAUSAL])
+def test_long_sequence_shape(mask_kind):
+    """From 16K queries the forward runs eight waves per workgroup: a ragged
+    16K+ sequence checked on sampled rows (start, end, random)."""
+    w = synth.small_workload(1, 2, 16411, 128, BF, mask_kind, seed=3700 + mask_kind, backward=False)
+    inp = synth.make_inputs(w)
+    t = to_device(inp)
+    announce(f"fa_fwd long shape N{w.N} mask{mask_kind}")
+    o, lse = fa.forward(t["q"], t["k"], t["v"], None, mask_kind)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3701)
+    rows = np.unique(np.concatenate([np.arange(200), np.arange(w.N - 200, w.N), rng.choice(w.N, 200, replace=False)]))
+    for h in range(w.H):
+        O, L = oracle.forward_head(inp.q[0, h], inp.k[0, h], inp.v[0, h], w.scale, mask_kind, rows=rows)
+        check_forward(o[0, h].float().cpu().numpy()[rows], lse[0, h].cpu().numpy()[rows], O, L, BF, f"head {h}")
