@@ -44,6 +44,7 @@ import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 2516.6: 256 CUs x 2.4 GHz x 4096 FLOP/clk
 PEAK_F32_VALU_TFLOPS = 157.3
+PEAK_FP8_TFLOPS = 256 * 2.4e9 * 8192 / 1e12      # 5033.2: the published dense FP8 MFMA peak (5.0 PFLOP/s)
 A100_FIG2_MS = 7.3                                # the pages' GPT-2-medium attention runtime (context)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "rowterm": "bwd_rowterm_bf16_kernel",
@@ -196,7 +197,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gpt2_medium", choices=sorted(synth.WORKLOADS) + sorted(synth.PACKED_WORKLOADS))
+    ap.add_argument("--workload", default="gpt2_medium",
+                    choices=sorted(synth.WORKLOADS) + sorted(synth.PACKED_WORKLOADS) + sorted(synth.FP8_WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
@@ -232,6 +234,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.workload in synth.PACKED_WORKLOADS:
         return run_packed(args, synth.PACKED_WORKLOADS[args.workload], dev)
+    if args.workload in synth.FP8_WORKLOADS:
+        return run_fp8(args, synth.FP8_WORKLOADS[args.workload], dev)
     w = synth.WORKLOADS[args.workload]
     backward = w.backward
     print(f"# workload {w.name}: B{w.B} H{w.H} N{w.N} d{w.d} dtype{w.dtype} mask{w.mask_kind} "
@@ -501,6 +505,83 @@ def run_packed(args, w: synth.PackedWorkload, dev) -> int:
         "roofline": {"kernel": KERNEL_NAMES["fwd"], "bound": "mfma", "achieved": round(fwd_tf, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "flop_per_launch": fwd_flop, "mean_launch_ms": round(float(fwd_ms.mean()), 4)},
+        "cpu_baseline": cpu,
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def run_fp8(args, w: synth.Workload, dev) -> int:
+    """FP8 (E4M3) forward: fa_fwd_fp8 per step on codes drawn by
+    synth.fp8_inputs (V transposed); FLOPs 4*d*vis per head."""
+    import torch
+    import io_aware_exact_10_amd as fa
+
+    print(f"# workload {w.name}: B{w.B} H{w.H} N{w.N} d{w.d} fp8 mask{w.mask_kind} fwd", file=sys.stderr, flush=True)
+    f = synth.fp8_inputs(w.B, w.H, w.N, w.d, w.seed)
+    q8, k8, vt8 = (torch.from_numpy(x).to(dev) for x in (f.q8, f.k8, f.vt8))
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def fwd():
+        fa.forward_fp8(q8, k8, vt8, f.q_descale, f.k_descale, f.v_descale, w.scale, w.mask_kind, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    vis = visible_pairs(w, None)
+    flop = 4.0 * w.d * vis * w.B * w.H
+    tf = flop / (ms * 1e-3) / 1e12
+    print(f"# timed {args.steps} steps: {ms:.4f} ms/step, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        print("# timing the CPU oracle sample", file=sys.stderr, flush=True)
+        rows = np.arange(2048) if w.N > 8192 else None
+        t1 = time.perf_counter()
+        done, flops = 0, 0.0
+        for b in range(w.B):
+            for h in range(w.H):
+                oracle.forward_head(f.q[b, h], f.k[b, h], f.v[b, h], w.scale, w.mask_kind, rows=rows)
+                done += 1
+                if rows is None:
+                    flops += flop / (w.B * w.H)
+                else:
+                    flops += 4.0 * w.d * rows.size * (rows.size + 1) / 2
+                if time.perf_counter() - t1 > args.cpu_budget:
+                    break
+            if time.perf_counter() - t1 > args.cpu_budget:
+                break
+        el = time.perf_counter() - t1
+        cpu = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{done} of {w.B * w.H} heads" + (", query rows 0..2047" if rows is not None else ""),
+               "seconds": round(el, 2)}
+
+    mask_name = {0: "none", 1: "causal"}[w.mask_kind]
+    rec = {
+        "metric": "attention fwd / fwd+bwd TFLOP/s and % of bf16 MFMA peak, N=1k-32k, d=64/128",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic: Q, K, V ~ N(0,1) seeded, quantized to OCP E4M3 with descale 2^-4; V transposed",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} mask={mask_name} fwd, E4M3 inputs, bf16 O",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": mask_name, "pass": "fwd", "seed": w.seed},
+        "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": "fwd_fp8_kernel", "bound": "mfma", "achieved": round(tf, 2),
+                     "peak": round(PEAK_FP8_TFLOPS, 1), "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None, "flop_per_launch": flop, "mean_launch_ms": round(ms, 4)},
         "cpu_baseline": cpu,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }

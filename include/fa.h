@@ -233,6 +233,35 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int total_q, int total_k, int d, float scale, int mask_kind, int dtype, int num_splits,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * FP8 forward: the forward pass on 8-bit floating-point inputs, the variant
+ * "Flash Attention — Revolutionizing Transformer Efficiency Through
+ * Memory-Aware Algorithms", "Flash Attention 3 (2024)" lists (FP8 support),
+ * on the gfx950 FP8 matrix instructions (twice the bf16 rate).
+ *
+ * Inputs. q, k: [B, H, N, d] bytes; v_t: V transposed, [B, H, d, ldv] bytes
+ *   (v_t[b][h][j][n] = V[b][h][n][j]; columns N .. ldv-1 are padding and may
+ *   hold anything). Every byte is an OCP E4M3 code (1 sign, 4 exponent bits
+ *   with bias 7, 3 mantissa bits; largest finite 448; S.1111.111 is NaN). The
+ *   represented tensors are Q = q_descale * q, K = k_descale * k,
+ *   V = v_descale * v.
+ * Outputs. o: bf16 [B, H, N, d]; lse: float [B, H, N], as for fa_fwd with
+ *   the represented tensors.
+ * Arithmetic. Scores are exact products of the codes accumulated in fp32,
+ *   times scale * q_descale * k_descale. The probabilities are rounded to
+ *   E4M3 for the P.V product; the row sums and the LSE use them unrounded.
+ * Supported. d in {64, 128}; mask_kind FA_MASK_NONE or FA_MASK_CAUSAL
+ *   (N_q = N_k); ldv >= N and a multiple of 16; finite scale and descale
+ *   factors whose product is finite.
+ * Errors. As for fa_fwd: FA_ERR_NULL, FA_ERR_SHAPE (also a bad ldv),
+ *   FA_ERR_UNSUPPORTED (d), FA_ERR_MASK (block-sparse or unknown),
+ *   FA_ERR_ARG (non-finite factor, overlapping output), FA_ERR_ALIGN
+ *   (q, k, v_t, o 16-byte, lse 4-byte), FA_ERR_HIP.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* lse,
+               int B, int H, int N, int d, int ldv, float scale,
+               float q_descale, float k_descale, float v_descale, int mask_kind, hipStream_t stream);
+
 /* Static, human-readable name of a fa_status value ("unknown status" otherwise). */
 const char* fa_status_string(int status);
 

@@ -31,7 +31,8 @@ __all__ = [
     "FAError", "fa_fwd", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen", "fa_bwd_varlen",
     "fa_bwd_varlen_workspace_bytes", "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
-    "forward", "backward", "forward_varlen", "backward_varlen", "forward_splitkv", "library_path", "lib",
+    "fa_fwd_fp8", "forward", "backward", "forward_varlen", "backward_varlen", "forward_splitkv", "forward_fp8",
+    "library_path", "lib",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.fa_splitkv_workspace_bytes.restype = sz
         L.fa_fwd_splitkv.argtypes = [vp] * 7 + [i] * 8 + [f, i, i, i, vp, sz, vp]
         L.fa_fwd_splitkv.restype = i
+        L.fa_fwd_fp8.argtypes = [vp] * 5 + [i] * 5 + [f, f, f, f, i, vp]
+        L.fa_fwd_fp8.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -103,7 +106,7 @@ def declared_functions() -> list[str]:
     """Names of the functions include/fa.h declares."""
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", txt)))
 
 
 # ---------------------------------------------------------------------------
@@ -177,6 +180,13 @@ def fa_fwd_splitkv(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, Hkv, max_s
     return int(lib().fa_fwd_splitkv(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, Hkv, max_seqlen_q,
                                     max_seqlen_k, total_q, total_k, d, ctypes.c_float(scale), mask_kind, dtype,
                                     num_splits, workspace, workspace_bytes, stream))
+
+
+def fa_fwd_fp8(q, k, v_t, o, lse, B, H, N, d, ldv, scale, q_descale, k_descale, v_descale, mask_kind,
+               stream) -> int:
+    return int(lib().fa_fwd_fp8(q, k, v_t, o, lse, B, H, N, d, ldv, ctypes.c_float(scale),
+                                ctypes.c_float(q_descale), ctypes.c_float(k_descale), ctypes.c_float(v_descale),
+                                mask_kind, stream))
 
 
 # ---------------------------------------------------------------------------
@@ -371,4 +381,30 @@ def forward_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
                         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_splitkv")
+    return o, lse
+
+
+def forward_fp8(q, k, v_t, q_descale=1.0, k_descale=1.0, v_descale=1.0, scale=None, mask_kind=MASK_NONE,
+                out=None, lse=None):
+    """FP8 (E4M3) forward on the current stream; returns (o bf16, lse fp32).
+
+    q, k: uint8 [B, H, N, d] E4M3 codes; v_t: uint8 [B, H, d, ldv], V
+    transposed (ldv >= N, a multiple of 16). scale defaults to 1/sqrt(d).
+    """
+    for t in (q, k, v_t):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v_t must be contiguous uint8 (E4M3 code) GPU tensors of rank 4")
+    if q.shape != k.shape:
+        raise ValueError("q and k must have the same shape")
+    B, H, N, d = q.shape
+    if tuple(v_t.shape[:3]) != (B, H, d):
+        raise ValueError("v_t must be [B, H, d, ldv]")
+    ldv = v_t.shape[3]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v_t.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, ldv,
+                    scale, float(q_descale), float(k_descale), float(v_descale), mask_kind, _stream(q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
     return o, lse

@@ -445,3 +445,50 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) forward, dense layout
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* lse,
+               int B, int H, int N, int d, int ldv, float scale,
+               float q_descale, float k_descale, float v_descale, int mask_kind, hipStream_t stream) {
+  if (!q || !k || !v_t || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if ((int64_t)B * H * N > kMaxElems / 128) return FA_ERR_SHAPE;
+  if ((int64_t)B * H * (((int64_t)N + 127) / 128) >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  if (ldv < N || ldv % 16 != 0 || (int64_t)ldv * 128 >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return FA_ERR_ARG;
+  const float sk = scale * q_descale * k_descale;
+  if (!isfinite(sk)) return FA_ERR_ARG;
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL) return FA_ERR_MASK;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v_t, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  const size_t heads = (size_t)B * H;
+  const size_t qb = heads * N * d, vb = heads * d * (size_t)ldv, ob = heads * N * d * 2, lb = heads * N * 4;
+  const void* ins[3] = {q, k, v_t};
+  const size_t insz[3] = {qb, qb, vb};
+  for (int j = 0; j < 3; ++j)
+    if (overlap(o, ob, ins[j], insz[j]) || overlap(lse, lb, ins[j], insz[j])) return FA_ERR_ARG;
+  if (overlap(o, ob, lse, lb)) return FA_ERR_ARG;
+  fa::AttnParams p = {};
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.c = fabsf(sk) * 1.4426950408889634f;
+  p.qflip = sk < 0.f ? 0x80808080u : 0u;   // E4M3 sign bit of every Q byte
+  p.ldv = ldv;
+  p.vscale = v_descale;
+  p.q = q;
+  p.k = k;
+  p.v = v_t;
+  p.o = o;
+  p.lse = lse;
+  return fa::launch_fwd_fp8(p, mask_kind, stream) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

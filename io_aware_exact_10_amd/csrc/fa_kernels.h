@@ -46,6 +46,10 @@ struct AttnParams {
   int splits;
   float* part_o;
   float* part_lse;
+  // FP8 forward: V is given transposed, [B, H, d, ldv] bytes; O is scaled
+  // by vscale (the V descale factor).
+  int ldv;
+  float vscale;
 };
 
 // Per-sequence view used by the kernels: lengths and the element offsets of
@@ -90,6 +94,8 @@ enum BwdStep { kBwdRowterm = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7 };
 int launch_fwd_bf16(const AttnParams& p, int mask_kind, hipStream_t stream);
 int launch_bwd_bf16(const AttnParams& p, int mask_kind, int steps, hipStream_t stream);
 int launch_fwd_f32(const AttnParams& p, int mask_kind, hipStream_t stream);
+// FP8 (E4M3) forward, dense layout, bf16 O.
+int launch_fwd_fp8(const AttnParams& p, int mask_kind, hipStream_t stream);
 // Split-key forward of a packed batch (partial ranges, then the merge).
 int launch_splitkv_bf16(const AttnParams& p, int mask_kind, hipStream_t stream);
 int launch_bwd_f32(const AttnParams& p, int mask_kind, int steps, hipStream_t stream);

@@ -247,3 +247,82 @@ PACKED_WORKLOADS = {
     # 1024..8192 keys, 32 query heads over 8 K/V heads, d = 128.
     "decode_splitkv": PackedWorkload("decode_splitkv", 64, 8192, 32, 8, 128, MASK_CAUSAL, False, 7, queries=1),
 }
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) codes: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no
+# infinities; S.1111.111 is NaN; largest finite 448, smallest subnormal 2^-9.
+# ---------------------------------------------------------------------------
+def fp8_e4m3_table() -> np.ndarray:
+    """float32 value of each of the 256 E4M3 codes (NaN for 0x7F, 0xFF)."""
+    codes = np.arange(256)
+    s = np.where(codes & 0x80, -1.0, 1.0)
+    e = (codes >> 3) & 15
+    m = codes & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    vals = (s * mag).astype(np.float32)
+    vals[(e == 15) & (m == 7)] = np.nan
+    return vals
+
+
+_E4M3 = fp8_e4m3_table()
+_E4M3_POS = _E4M3[:0x7F].astype(np.float64)      # codes 0x00..0x7E: 0 .. 448, increasing
+
+
+def fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """float -> E4M3 codes (uint8), round to nearest, ties to the even code.
+    Values beyond +-448 (and NaN) are rejected: callers scale into range."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.isfinite(x).all() or np.abs(x).max(initial=0.0) > 448.0:
+        raise ValueError("E4M3 input out of range")
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a), 1, 0x7E)
+    lo = hi - 1
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def fp8_to_f32(bits: np.ndarray) -> np.ndarray:
+    """E4M3 codes (uint8) -> their exact float32 values."""
+    return _E4M3[np.asarray(bits, dtype=np.uint8)]
+
+
+@dataclasses.dataclass
+class Fp8Inputs:
+    """FP8 inputs of one dense workload: codes q8, k8 [B, H, N, d] and
+    vt8 [B, H, d, ldv] (V transposed, columns N..ldv-1 padding), their
+    descale factors, and the dequantized fp32 values q, k, v [B, H, N, d]
+    (exactly what the codes times the factors represent)."""
+    q8: np.ndarray
+    k8: np.ndarray
+    vt8: np.ndarray
+    ldv: int
+    q_descale: float
+    k_descale: float
+    v_descale: float
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+
+
+def fp8_inputs(B, H, N, d, seed, descale=2.0 ** -4, pad_code=0) -> Fp8Inputs:
+    """Draw Q, K, V ~ N(0, 1) (seeded, in that order), quantize x / descale to
+    E4M3 with one descale factor per tensor, and lay V out transposed with a
+    leading dimension rounded up to 16 bytes (padding filled with pad_code)."""
+    q, k, v = normal_tensors(seed, (B, H, N, d), 3)
+    codes = [fp8_e4m3_bits(t / descale) for t in (q, k, v)]
+    ldv = -(-N // 16) * 16
+    vt8 = np.full((B, H, d, ldv), pad_code, dtype=np.uint8)
+    vt8[..., :N] = np.swapaxes(codes[2], 2, 3)
+    deq = [fp8_to_f32(c) * np.float32(descale) for c in codes]
+    return Fp8Inputs(codes[0], codes[1], vt8, ldv, descale, descale, descale, *deq)
+
+
+# FP8 forward workloads: the bf16 causal shapes with E4M3 inputs (per-tensor
+# descale 2^-4), forward only.
+FP8_WORKLOADS = {
+    "causal_train_fp8": Workload("causal_train_fp8", 8, 16, 4096, 128, DTYPE_BF16, MASK_CAUSAL, False, 3),
+    "long_prefill_fp8": Workload("long_prefill_fp8", 1, 32, 32768, 128, DTYPE_BF16, MASK_CAUSAL, False, 4),
+}

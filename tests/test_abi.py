@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen",
                           "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_splitkv_splits",
-                          "fa_splitkv_workspace_bytes", "fa_fwd_splitkv"}
+                          "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_fp8"}
     L = fa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -301,3 +301,28 @@ def test_splitkv_split_choice_and_workspace():
 ])
 def test_splitkv_validation(kw, code):
     assert fa.fa_fwd_splitkv(**skv_args(**kw)) == code
+
+
+# --------------------------------------------------------------------------
+# FP8 forward
+# --------------------------------------------------------------------------
+def f8_args(**kw):
+    q, k, vt, o, lse = ptrs(5)
+    args = dict(q=q, k=k, v_t=vt, o=o, lse=lse, B=1, H=2, N=100, d=128, ldv=112, scale=0.088,
+                q_descale=0.0625, k_descale=0.0625, v_descale=0.0625, mask_kind=fa.MASK_CAUSAL, stream=None)
+    args.update(kw)
+    return args
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(v_t=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(N=0), fa.FA_ERR_SHAPE), (dict(ldv=96), fa.FA_ERR_SHAPE), (dict(ldv=120), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask_kind=fa.MASK_BLOCK_SPARSE), fa.FA_ERR_MASK), (dict(mask_kind=5), fa.FA_ERR_MASK),
+    (dict(scale=math.nan), fa.FA_ERR_ARG), (dict(v_descale=math.inf), fa.FA_ERR_ARG),
+    (dict(q_descale=1e30, k_descale=1e30), fa.FA_ERR_ARG),        # product overflows
+    (dict(k=BIG + A + 8), fa.FA_ERR_ALIGN), (dict(lse=4 * BIG + A + 1), fa.FA_ERR_ALIGN),
+    (dict(o=A + 2 * BIG), fa.FA_ERR_ARG),                           # o aliases v_t
+])
+def test_fp8_validation(kw, code):
+    assert fa.fa_fwd_fp8(**f8_args(**kw)) == code

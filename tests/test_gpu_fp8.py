@@ -1,0 +1,162 @@
+"""GPU parity of the FP8 (E4M3) forward (fa_fwd_fp8) through the C ABI
+against the CPU float64 oracle run on the represented (dequantized) tensors.
+
+Tolerances. The FP8 matrix instruction forms each product of two codes
+exactly but does not add a 64-term dot product exactly: a probe of the
+instruction (256 + 63 * 2^-6 came out 256.875) shows the sum keeping about
+12 bits below its largest product. That adds at most 2^-9 x the largest
+|product| of each 64-key tile to O (and likewise to the scores). The LSE
+keeps the bf16 path's bound, 1e-3, for these inputs (products of N(0, 1)
+codes stay far below the level where that term reaches it). O also differs
+from the definition by the rounding of P to E4M3 (relative half-spacing 2^-4
+in the normal range) and the bf16 rounding of O:
+  * where the probabilities are exactly representable (integer log2 scores,
+    at most 9 below the row max) only the bf16 rounding of O and the
+    instruction's sums remain: |dO| <= 2^-8 |O| + 2^-9 sum over tiles of
+    max_j P_ij |V_jd| + 1e-6;
+  * for N(0, 1) inputs the rounding errors of the weights are independent
+    and of mean zero, so the relative Frobenius error of O is about the rms
+    relative rounding error 2^-4 / sqrt(3) = 0.036: bound 0.05; and no
+    element may exceed 2^-4 max|V|, the error if every weight's rounding had
+    the same sign.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_10_amd as fa
+import oracle
+import synth
+from gpu_util import announce, max_abs
+
+pytestmark = pytest.mark.gpu
+
+NONE, CAUSAL = synth.MASK_NONE, synth.MASK_CAUSAL
+LSE_TOL = 1e-3
+FRO_TOL = 0.05
+
+
+def run_fp8(f, mask_kind, scale=None, q8=None, k8=None, vt8=None):
+    q8 = f.q8 if q8 is None else q8
+    k8 = f.k8 if k8 is None else k8
+    vt8 = f.vt8 if vt8 is None else vt8
+    B, H, N, d = q8.shape
+    t = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (q8, k8, vt8)]
+    announce(f"fa_fwd_fp8 B{B} H{H} N{N} d{d} ldv{vt8.shape[3]} mask{mask_kind} scale{scale}")
+    o, lse = fa.forward_fp8(*t, f.q_descale, f.k_descale, f.v_descale, scale, mask_kind)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_fp8(q, k, v, mask_kind, scale):
+    O, L = oracle.forward(q, k, v, scale, mask_kind)
+    return O.reshape(q.shape), L.reshape(q.shape[:3])
+
+
+def check_random(got, ref, v, what):
+    o, lse = got
+    O, L = ref
+    el = max_abs(lse, L)
+    assert el <= LSE_TOL, f"{what}: max|dLSE| = {el:.3g}"
+    eo = max_abs(o, O)
+    assert eo <= 2.0 ** -4 * float(np.abs(v).max()), f"{what}: max|dO| = {eo:.3g}"
+    fro = float(np.linalg.norm(o - O) / max(np.linalg.norm(O), 1e-12))
+    assert fro <= FRO_TOL, f"{what}: relative Frobenius error {fro:.3g}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask_kind", [NONE, CAUSAL])
+@pytest.mark.parametrize("N", [1, 17, 64, 127, 129, 300, 1000])
+def test_fp8_parity(N, mask_kind, d):
+    f = synth.fp8_inputs(1, 2, N, d, seed=8000 + N + d + mask_kind)
+    scale = 1.0 / math.sqrt(d)
+    check_random(run_fp8(f, mask_kind, scale), oracle_fp8(f.q, f.k, f.v, mask_kind, scale), f.v,
+                 f"N{N} d{d} mask{mask_kind}")
+
+
+def exact_p_inputs(N, d, seed):
+    """Q = e_0, K = b_j e_0 with integer b_j in [-9, 0] and scale chosen so
+    that the exp2-domain scores are b_j: every probability is a power of two
+    at most 9 below the row maximum, exactly representable in E4M3."""
+    f = synth.fp8_inputs(1, 2, N, d, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    q8 = np.zeros_like(f.q8)
+    q8[..., 0] = synth.fp8_e4m3_bits(np.array([1.0]))[0]
+    k8 = np.zeros_like(f.k8)
+    b = rng.integers(-9, 1, size=f.k8.shape[:3]).astype(np.float64)
+    k8[..., 0] = synth.fp8_e4m3_bits(b)
+    scale = float(np.float32(1.0 / (f.q_descale * f.k_descale * math.log2(math.e))))
+    q = synth.fp8_to_f32(q8) * np.float32(f.q_descale)
+    k = synth.fp8_to_f32(k8) * np.float32(f.k_descale)
+    return f, q8, k8, q, k, scale
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask_kind", [NONE, CAUSAL])
+@pytest.mark.parametrize("N", [33, 200, 513])
+def test_fp8_exact_probabilities(N, mask_kind, d):
+    """P exact in E4M3: only the bf16 rounding of O remains, so the key
+    permutation, the transposed V and the masking are checked tightly."""
+    f, q8, k8, q, k, scale = exact_p_inputs(N, d, seed=8100 + N + d + mask_kind)
+    o, lse = run_fp8(f, mask_kind, scale, q8=q8, k8=k8)
+    O, L = oracle_fp8(q, k, f.v, mask_kind, scale)
+    assert max_abs(lse, L) <= LSE_TOL
+    for h in range(q.shape[1]):
+        P = oracle.probabilities_head(q[0, h], k[0, h], scale, mask_kind)
+        term = np.zeros((N, d))
+        for t0 in range(0, N, 64):                        # one 64-key product per tile
+            pv = P[:, t0:t0 + 64, None] * np.abs(f.v[0, h, t0:t0 + 64])[None]
+            term += pv.max(axis=1)
+        bound = 2.0 ** -8 * np.abs(O[0, h]) + 2.0 ** -9 * term + 1e-6
+        err = np.abs(o[0, h] - O[0, h])
+        assert (err <= bound).all(), float((err / bound).max())
+
+
+@pytest.mark.parametrize("mask_kind", [NONE, CAUSAL])
+def test_fp8_zero_queries(mask_kind):
+    """Q = 0: every probability is 1, so O is the mean of the visible V rows
+    (prefix means when causal) and LSE = ln(count)."""
+    N, d = 300, 128
+    f = synth.fp8_inputs(1, 1, N, d, seed=8200)
+    o, lse = run_fp8(f, mask_kind, 0.1, q8=np.zeros_like(f.q8))
+    v = f.v[0, 0].astype(np.float64)
+    if mask_kind == CAUSAL:
+        ref = np.cumsum(v, axis=0) / np.arange(1, N + 1)[:, None]
+        cnt = np.arange(1, N + 1)
+    else:
+        ref = np.broadcast_to(v.mean(axis=0), v.shape)
+        cnt = np.full(N, N)
+    assert (np.abs(o[0, 0] - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5).all()
+    assert np.abs(lse[0, 0] - np.log(cnt)).max() <= 1e-5
+
+
+def test_fp8_padding_is_ignored():
+    """V^T columns past N hold NaN codes: the result is bitwise that of zero
+    padding."""
+    f = synth.fp8_inputs(2, 2, 77, 64, seed=8300)
+    fn = synth.fp8_inputs(2, 2, 77, 64, seed=8300, pad_code=0x7F)
+    a = run_fp8(f, NONE)
+    b = run_fp8(fn, NONE)
+    assert np.isfinite(b[0]).all()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0])
+def test_fp8_scale_sign_and_zero(scale):
+    f = synth.fp8_inputs(1, 2, 250, 128, seed=8400)
+    for mk in (NONE, CAUSAL):
+        check_random(run_fp8(f, mk, scale), oracle_fp8(f.q, f.k, f.v, mk, scale), f.v, f"scale {scale}")
+
+
+def test_fp8_workload_sampled_heads():
+    """The causal N = 4096, d = 128 workload in FP8 (B = 8, H = 16): whole
+    batch on the GPU, the oracle on sampled heads."""
+    B, H, N, d = 8, 16, 4096, 128
+    f = synth.fp8_inputs(B, H, N, d, seed=9)
+    o, lse = run_fp8(f, CAUSAL, 1.0 / math.sqrt(d))
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    for b, h in ((0, 0), (B - 1, H - 1), (3, 7)):
+        O, L = oracle.forward_head(f.q[b, h], f.k[b, h], f.v[b, h], 1.0 / math.sqrt(d), CAUSAL)
+        check_random((o[b, h], lse[b, h]), (O, L), f.v[b, h], f"head ({b},{h})")

@@ -1,5 +1,6 @@
 """The seeded input generator (CPU only)."""
 import numpy as np
+import pytest
 
 import synth
 
@@ -61,3 +62,41 @@ def test_workload_table():
     assert w["long_prefill"].backward is False
     assert w["tiny_f32"].dtype == synth.DTYPE_F32
     assert abs(w["causal_train"].scale - 128 ** -0.5) < 1e-15
+
+
+def test_fp8_e4m3_table_matches_the_format_definition():
+    """OCP 8-bit floating point E4M3: bias 7, 3 mantissa bits, no infinities,
+    S.1111.111 NaN, largest finite 448 = 1.75 * 2^8, smallest normal 2^-6,
+    smallest subnormal 2^-9."""
+    t = synth.fp8_e4m3_table()
+    assert t[0x38] == 1.0 and t[0x7E] == 448.0 and t[0x08] == 2.0 ** -6 and t[0x01] == 2.0 ** -9
+    assert t[0x07] == 7 * 2.0 ** -9 and t[0x40] == 2.0 and t[0x3F] == 1.875
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and np.isnan(t).sum() == 2
+    assert t[0x80] == 0.0 and np.signbit(t[0x80])
+    assert (t[0x80:0xFF] == -t[0x00:0x7F]).all()
+    pos = t[:0x7F]
+    assert (np.diff(pos) > 0).all()                      # codes ordered by value
+
+
+def test_fp8_encode_rounds_to_nearest_even():
+    t = synth.fp8_e4m3_table()
+    # exact values round-trip
+    codes = np.array([c for c in range(256) if not np.isnan(t[c])], dtype=np.uint8)
+    assert (synth.fp8_e4m3_bits(t[codes]) == codes).all()
+    # midpoints go to the even code; anything else to the nearest
+    for c in range(0x00, 0x7E):
+        mid = (float(t[c]) + float(t[c + 1])) / 2
+        assert synth.fp8_e4m3_bits(np.array([mid]))[0] == (c if c % 2 == 0 else c + 1)
+        assert synth.fp8_e4m3_bits(np.array([np.nextafter(mid, 0)]))[0] == c
+        assert synth.fp8_e4m3_bits(np.array([np.nextafter(mid, 1e9)]))[0] == c + 1
+    assert synth.fp8_e4m3_bits(np.array([-1.0625]))[0] == 0xB8
+    with pytest.raises(ValueError):
+        synth.fp8_e4m3_bits(np.array([449.0]))
+
+
+def test_fp8_inputs_layout():
+    f = synth.fp8_inputs(2, 3, 37, 64, seed=9, pad_code=0x7F)
+    assert f.ldv == 48 and f.vt8.shape == (2, 3, 64, 48)
+    assert (f.vt8[..., 37:] == 0x7F).all()
+    assert np.array_equal(np.swapaxes(f.vt8[..., :37], 2, 3), synth.fp8_e4m3_bits(f.v / f.v_descale))
+    assert np.array_equal(f.q, synth.fp8_to_f32(f.q8) * np.float32(f.q_descale))
