@@ -160,3 +160,17 @@ def test_fp8_workload_sampled_heads():
     for b, h in ((0, 0), (B - 1, H - 1), (3, 7)):
         O, L = oracle.forward_head(f.q[b, h], f.k[b, h], f.v[b, h], 1.0 / math.sqrt(d), CAUSAL)
         check_random((o[b, h], lse[b, h]), (O, L), f.v[b, h], f"head ({b},{h})")
+
+
+@pytest.mark.parametrize("mask_kind", [NONE, CAUSAL])
+def test_fp8_long_sequence_shape(mask_kind):
+    """A ragged 16K+ sequence (many query tiles, long key loop) checked on
+    sampled rows."""
+    N, d = 16411, 128
+    f = synth.fp8_inputs(1, 2, N, d, seed=8500 + mask_kind)
+    o, lse = run_fp8(f, mask_kind, 1.0 / math.sqrt(d))
+    rng = np.random.default_rng(8501)
+    rows = np.unique(np.concatenate([np.arange(200), np.arange(N - 200, N), rng.choice(N, 200, replace=False)]))
+    for h in range(2):
+        O, L = oracle.forward_head(f.q[0, h], f.k[0, h], f.v[0, h], 1.0 / math.sqrt(d), mask_kind, rows=rows)
+        check_random((o[0, h][rows], lse[0, h][rows]), (O, L), f.v[0, h], f"long head {h}")
