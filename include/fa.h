@@ -66,7 +66,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,        /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,       /* B, H or N < 1, or the element count overflows */
-  FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}, or an unknown dtype */
+  FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}, a dtype the call does not take, or too many split-key rows */
   FA_ERR_MASK = -4,        /* unknown mask_kind, or block_mask NULL for a block-sparse call */
   FA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_ALIGN = -6,       /* a pointer is not aligned as stated above */

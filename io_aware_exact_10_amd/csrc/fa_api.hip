@@ -82,7 +82,9 @@ const char* fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and the sizes must fit)";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype (d must be 64 or 128; dtype bf16 or f32)";
+    case FA_ERR_UNSUPPORTED:
+      return "unsupported configuration (d must be 64 or 128; dtype as the entry point allows; split-key: "
+             "(H / Hkv) * max_seqlen_q <= 128)";
     case FA_ERR_MASK: return "invalid mask (unknown mask_kind, or block_mask NULL for block-sparse)";
     case FA_ERR_WORKSPACE: return "workspace NULL or smaller than fa_bwd_workspace_bytes()";
     case FA_ERR_ALIGN: return "misaligned pointer (tensors 16-byte, lse 4-byte aligned)";
