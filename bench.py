@@ -48,12 +48,41 @@ PEAK_FP8_TFLOPS = 256 * 2.4e9 * 8192 / 1e12      # 5033.2: the published dense F
 A100_FIG2_MS = 7.3                                # the pages' GPT-2-medium attention runtime (context)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "rowterm": "bwd_rowterm_bf16_kernel",
-                "dkdv": "bwd_dkdv_bf16_kernel", "dq": "bwd_dq_bf16_kernel"}
+                "dkdv": "bwd_dkdv_bf16_kernel", "dq": "bwd_dq_bf16_kernel",
+                "splitkv": "splitkv_bf16_kernel", "combine": "splitkv_combine_kernel", "fwd_fp8": "fwd_fp8_kernel"}
 _CSRC = "io_aware_exact_10_amd/csrc/"
 KERNEL_SOURCES = {"fwd": (_CSRC + "fa_fwd_bf16.hip", _CSRC + "fa_common.h"),
                   "rowterm": (_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_common.h"),
                   "dkdv": (_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_common.h"),
-                  "dq": (_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_common.h")}
+                  "dq": (_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_common.h"),
+                  "splitkv": (_CSRC + "fa_splitkv_bf16.hip", _CSRC + "fa_common.h"),
+                  "combine": (_CSRC + "fa_splitkv_bf16.hip", _CSRC + "fa_common.h"),
+                  "fwd_fp8": (_CSRC + "fa_fwd_fp8.hip", _CSRC + "fa_common.h")}
+
+
+def measured_traffic(workload: str, key: str):
+    """HBM bytes per launch of kernel `key` on `workload` from the committed
+    counter summary, or None when absent or taken on other kernel source."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    rec = json.load(open(PROFILE_TRAFFIC)).get(workload, {}).get(key)
+    if rec and rec.get("source_digest") == source_digest(*KERNEL_SOURCES[key]):
+        return rec.get("hbm_bytes_per_launch")
+    return None
+
+
+def copy_calibration(nbytes: int, dev) -> None:
+    """One device-to-device copy of nbytes: the reference dispatch the
+    FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    if not nbytes:
+        return
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def visible_pairs(w: synth.Workload, mask: np.ndarray | None) -> int:
@@ -129,7 +158,9 @@ def naive_step(q, k, v, do, scale, mask_kind, bool_mask, backward):
 # rocprofv3 summaries (text for profiles/), read from the SQLite output
 # ---------------------------------------------------------------------------
 KEYS_BY_SUBSTR = (("fwd_bf16_kernel", "fwd"), ("bwd_rowterm_bf16_kernel", "rowterm"),
-                  ("bwd_dkdv_bf16_kernel", "dkdv"), ("bwd_dq_bf16_kernel", "dq"))
+                  ("bwd_dkdv_bf16_kernel", "dkdv"), ("bwd_dq_bf16_kernel", "dq"),
+                  ("splitkv_bf16_kernel", "splitkv"), ("splitkv_combine_kernel", "combine"),
+                  ("fwd_fp8_kernel", "fwd_fp8"))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -209,6 +240,9 @@ def main() -> int:
                     help="HBM bytes per launch from FETCH_SIZE / WRITE_SIZE counter databases")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--update-traffic", action="store_true", help="write the result into profiles/traffic.json")
+    ap.add_argument("--sweep", action="store_true",
+                    help="fwd and fwd+bwd TFLOP/s over N = 1K..32K (B*N = 32K tokens, H = 16), d = 64/128, "
+                         "no mask and causal; one JSON line per point, then a markdown table")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -232,6 +266,8 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        return run_sweep(args, dev)
     if args.workload in synth.PACKED_WORKLOADS:
         return run_packed(args, synth.PACKED_WORKLOADS[args.workload], dev)
     if args.workload in synth.FP8_WORKLOADS:
@@ -310,11 +346,7 @@ def main() -> int:
     dom = max((n for n in names if n != "rowterm"), key=lambda n: per[n].mean())
     dom_t = float(per[dom].mean())
     achieved = kflop[dom] / (dom_t * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(PROFILE_TRAFFIC):
-        rec = json.load(open(PROFILE_TRAFFIC)).get(w.name, {}).get(dom)
-        if rec and rec.get("source_digest") == source_digest(*KERNEL_SOURCES[dom]):
-            traffic = rec.get("hbm_bytes_per_launch")
+    traffic = measured_traffic(w.name, dom)
     roofline = {"kernel": KERNEL_NAMES[dom],
                 "bound": "mfma" if w.dtype == synth.DTYPE_BF16 else "alu",
                 "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
@@ -346,13 +378,7 @@ def main() -> int:
             naive = {"error": repr(ex)[:200]}
         torch.cuda.empty_cache()
 
-    if args.copy_calibration:
-        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args.copy_calibration, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -448,6 +474,7 @@ def run_packed(args, w: synth.PackedWorkload, dev) -> int:
     step_ms = fwd_ms + bwd_ms
     print(f"# timed {args.steps} steps: {step_ms.mean():.3f} ms/step fwd {fwd_ms.mean():.3f} bwd {bwd_ms.mean():.3f}",
           file=sys.stderr, flush=True)
+    copy_calibration(args.copy_calibration, dev)
     if w.mask_kind == synth.MASK_CAUSAL:
         vis = sum(n * (n + 1) // 2 for n in lens)
     else:
@@ -504,11 +531,73 @@ def run_packed(args, w: synth.PackedWorkload, dev) -> int:
                 if w.backward else None),
         "roofline": {"kernel": KERNEL_NAMES["fwd"], "bound": "mfma", "achieved": round(fwd_tf, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "flop_per_launch": fwd_flop, "mean_launch_ms": round(float(fwd_ms.mean()), 4)},
+                     "traffic": measured_traffic(w.name, "fwd"), "flop_per_launch": fwd_flop,
+                     "mean_launch_ms": round(float(fwd_ms.mean()), 4)},
         "cpu_baseline": cpu,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }
     print(json.dumps(rec), flush=True)
+    return 0
+
+
+def run_sweep(args, dev) -> int:
+    """Sequence-length sweep at a fixed token count (B * N = 32768, H = 16):
+    seeded N(0, 1) bf16 inputs drawn on the device; forward and forward +
+    backward timed with HIP events (median over the timed steps)."""
+    import torch
+    import io_aware_exact_10_amd as fa
+
+    gen = torch.Generator(device=dev)
+    rows = []
+    for d in (64, 128):
+        for mask_kind in (synth.MASK_NONE, synth.MASK_CAUSAL):
+            for N in (1024, 2048, 4096, 8192, 16384, 32768):
+                B, H = 32768 // N, 16
+                gen.manual_seed(1000 * d + 10 * mask_kind + N)
+                q, k, v, do = (torch.randn((B, H, N, d), generator=gen, device=dev, dtype=torch.float32)
+                               .to(torch.bfloat16) for _ in range(4))
+                o = torch.empty_like(q)
+                lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+                dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+                ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+                scale = 1.0 / math.sqrt(d)
+
+                def fwd():
+                    fa.forward(q, k, v, scale, mask_kind, None, out=o, lse=lse)
+
+                def bwd():
+                    fa.backward(q, k, v, o, lse, do, scale, mask_kind, None, workspace=ws, dq=dq, dk=dk, dv=dv)
+
+                for _ in range(args.warmup):
+                    fwd()
+                    bwd()
+                torch.cuda.synchronize()
+                ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+                for i in range(args.steps):
+                    ev[i][0].record()
+                    fwd()
+                    ev[i][1].record()
+                    bwd()
+                    ev[i][2].record()
+                torch.cuda.synchronize()
+                f_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+                b_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+                vis = N * N if mask_kind == synth.MASK_NONE else N * (N + 1) // 2
+                fl = 4.0 * d * vis * B * H
+                rec = {"N": N, "B": B, "H": H, "d": d, "mask": "causal" if mask_kind else "none",
+                       "fwd_ms": round(f_ms, 4), "fwd_tflops": round(fl / (f_ms * 1e-3) / 1e12, 1),
+                       "fwd_frac": round(fl / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "fwdbwd_ms": round(f_ms + b_ms, 4),
+                       "fwdbwd_tflops": round(3.5 * fl / ((f_ms + b_ms) * 1e-3) / 1e12, 1)}
+                rows.append(rec)
+                print(json.dumps(rec), flush=True)
+                del q, k, v, do, o, lse, dq, dk, dv, ws
+                torch.cuda.empty_cache()
+    print("| d | mask | N | B | fwd ms | fwd TFLOP/s | % of bf16 peak | fwd+bwd ms | fwd+bwd TFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['d']} | {r['mask']} | {r['N']} | {r['B']} | {r['fwd_ms']} | {r['fwd_tflops']} | "
+              f"{100 * r['fwd_frac']:.1f} | {r['fwdbwd_ms']} | {r['fwdbwd_tflops']} |")
     return 0
 
 
@@ -540,6 +629,7 @@ def run_fp8(args, w: synth.Workload, dev) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    copy_calibration(args.copy_calibration, dev)
     vis = visible_pairs(w, None)
     flop = 4.0 * w.d * vis * w.B * w.H
     tf = flop / (ms * 1e-3) / 1e12
@@ -581,7 +671,8 @@ def run_fp8(args, w: synth.Workload, dev) -> int:
         "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
         "roofline": {"kernel": "fwd_fp8_kernel", "bound": "mfma", "achieved": round(tf, 2),
                      "peak": round(PEAK_FP8_TFLOPS, 1), "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None, "flop_per_launch": flop, "mean_launch_ms": round(ms, 4)},
+                     "traffic": measured_traffic(w.name, "fwd_fp8"), "flop_per_launch": flop,
+                     "mean_launch_ms": round(ms, 4)},
         "cpu_baseline": cpu,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }
@@ -633,6 +724,7 @@ def run_decode(args, w: synth.PackedWorkload, lens, qlens, dev) -> int:
     else:
         vis = sum(nq * nk for nq, nk in zip(qlens, lens))
     flop = 4.0 * w.d * vis * w.H
+    copy_calibration(args.copy_calibration, dev)
     hbm_bytes = 2 * Tk * w.Hkv * w.d * 2 + 2 * Tq * w.H * w.d * 2 + Tq * w.H * 4
     gbs = hbm_bytes / (ms * 1e-3) / 1e9
     print(f"# timed {args.steps} steps: {ms:.4f} ms/step, {gbs:.0f} GB/s, splits {splits}", file=sys.stderr,
@@ -672,7 +764,10 @@ def run_decode(args, w: synth.PackedWorkload, lens, qlens, dev) -> int:
         "hbm_gbs": round(gbs, 1),
         "roofline": {"kernel": "splitkv_bf16_kernel + splitkv_combine_kernel", "bound": "hbm",
                      "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(gbs / 8000.0, 4),
-                     "traffic": None, "bytes_per_launch": hbm_bytes, "mean_launch_ms": round(ms, 4)},
+                     "traffic": (None if measured_traffic(w.name, "splitkv") is None
+                                 or measured_traffic(w.name, "combine") is None
+                                 else measured_traffic(w.name, "splitkv") + measured_traffic(w.name, "combine")),
+                     "bytes_per_launch": hbm_bytes, "mean_launch_ms": round(ms, 4)},
         "cpu_baseline": cpu,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }

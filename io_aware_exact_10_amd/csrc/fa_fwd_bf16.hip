@@ -41,10 +41,10 @@ constexpr int kMaskBlock = 128;  // block-sparse mask granularity
 
 // Workgroup shape: NW waves of 32 query rows each, NBUF K/V tiles in LDS
 // (NBUF - 1 copies in flight while one tile is computed). Four waves by
-// default; from 16K queries on, eight waves (256 queries share every K/V
-// tile copied into LDS), 5 % faster at 32K. Double buffering in both: a
-// third buffer was measured slower. Block-sparse keeps four waves so a
-// workgroup's queries stay inside one 128-row mask block.
+// default; at d = 128 from 16K queries on, eight waves (256 queries share
+// every K/V tile copied into LDS), 5 % faster at 32K. Double buffering in
+// both: a third buffer was measured slower. Block-sparse keeps four waves so
+// a workgroup's queries stay inside one 128-row mask block.
 template <int D, int MASK, int NW_, int NBUF_>
 struct FwdShape {
   static constexpr int NW = NW_;
@@ -331,7 +331,7 @@ static int launch_fwd_s(const AttnParams& p, hipStream_t stream) {
 
 template <int D, int MASK>
 static int launch_fwd_t(const AttnParams& p, hipStream_t stream) {
-  if constexpr (MASK != 2) {
+  if constexpr (MASK != 2 && D == 128) {
     if (p.Nq >= FA_FWD_LONG_N) return launch_fwd_s<D, MASK, 8, FA_FWD_LONG_NBUF>(p, stream);
   }
   return launch_fwd_s<D, MASK, 4, 2>(p, stream);
