@@ -248,22 +248,30 @@ __global__ __launch_bounds__(256) void splitkv_combine_kernel(AttnParams p, uint
   // Ranges of this sequence (as laid out by the split kernel).
   const int per = ((p.Nk + BC - 1) / BC + p.splits - 1) / p.splits;
   const int S = (((sq.nk + BC - 1) / BC) + per - 1) / per;
+  // Range s's LSE sits in lane s % 64 (two per lane: at most 128 ranges);
+  // the max and the weight sum are wave reductions.
   const float* __restrict__ lp = p.part_lse + (int64_t)hq * p.Tq + tok;
   const int64_t lstride = (int64_t)p.H * p.Tq;
-  float m = -INFINITY;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, lp[s * lstride]);
-  float tot = 0.f, acc[CPL];
+  const float l0 = lane < S ? lp[lane * lstride] : -INFINITY;
+  const float l1 = lane + 64 < S ? lp[(lane + 64) * lstride] : -INFINITY;
+  float m = fmaxf(l0, l1);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const float w0 = m == -INFINITY ? 0.f : fast_exp2((l0 - m) * kLog2e);   // 0 for an empty range
+  const float w1 = m == -INFINITY ? 0.f : fast_exp2((l1 - m) * kLog2e);
+  float tot = w0 + w1;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+  float acc[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
-  if (m != -INFINITY) {
-    const float* __restrict__ op = p.part_o + (tok * p.H + hq) * D + lane * CPL;
-    const int64_t ostride = (int64_t)p.Tq * p.H * D;
-    for (int s = 0; s < S; ++s) {
-      const float wgt = fast_exp2((lp[s * lstride] - m) * kLog2e);   // 0 for an empty range
-      tot += wgt;
+  const float* __restrict__ op = p.part_o + (tok * p.H + hq) * D + lane * CPL;
+  const int64_t ostride = (int64_t)p.Tq * p.H * D;
+#pragma unroll 4
+  for (int s = 0; s < S; ++s) {
+    const float wgt = __shfl(s < 64 ? w0 : w1, s & 63);
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) acc[j] += wgt * op[s * ostride + j];
-    }
+    for (int j = 0; j < CPL; ++j) acc[j] += wgt * op[s * ostride + j];
   }
   const float inv = tot > 0.f ? 1.0f / tot : 0.f;
   uint16_t* __restrict__ Orow = (uint16_t*)p.o + tok * p.q_rs + hq * p.q_hs + lane * CPL;
