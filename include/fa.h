@@ -88,8 +88,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int mask_kind, const uint8_t* block_mask, int dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: the float row term
- * D_i = sum_k dO_ik O_ik for every (b, h, i), rounded up to 256 bytes.
+ * Bytes of device workspace fa_bwd needs: two float arrays with one entry per
+ * query row (b, h, i), each rounded up to 256 bytes: the row term
+ * D_i = sum_k dO_ik O_ik and a rescaled copy of the LSE that the loops use.
  * Returns 0 if the shape is invalid.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
@@ -117,13 +118,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 /*
  * The three steps fa_bwd enqueues, callable one by one with the same
  * arguments and the same validation (arguments a step does not use are not
- * taken). fa_bwd_rowterm writes the row term D into the workspace;
+ * taken). fa_bwd_rowterm writes the row term D and the rescaled LSE into the
+ * workspace;
  * fa_bwd_dkdv and fa_bwd_dq each read it and are independent of each other,
  * so they may run on two streams once the row term is complete.
  * workspace has the size and alignment fa_bwd requires; for fa_bwd_dkdv and
  * fa_bwd_dq its contents must be those fa_bwd_rowterm left.
  */
-int fa_bwd_rowterm(const void* o, const void* dO, int B, int H, int N, int d, int dtype,
+int fa_bwd_rowterm(const void* o, const void* dO, const float* lse, int B, int H, int N, int d, int dtype,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
                 void* dk, void* dv, int B, int H, int N, int d, float scale,
@@ -180,8 +182,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   int total_q, int total_k, int d, float scale, int mask_kind,
                   int dtype, hipStream_t stream);
 
-/* Workspace bytes fa_bwd_varlen needs (the float row term [H, total_q],
- * rounded up to 256 bytes); 0 for an invalid shape. */
+/* Workspace bytes fa_bwd_varlen needs (two float arrays [H, total_q], the
+ * row term and the rescaled LSE, each rounded up to 256 bytes); 0 for an
+ * invalid shape. */
 size_t fa_bwd_varlen_workspace_bytes(int total_q, int H, int d);
 
 /*

@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd.restype = i
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
         L.fa_bwd.restype = i
-        L.fa_bwd_rowterm.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+        L.fa_bwd_rowterm.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
         L.fa_bwd_rowterm.restype = i
         L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
         L.fa_bwd_dkdv.restype = i
@@ -131,8 +131,8 @@ def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, mask_kind, block_
                             mask_kind, block_mask, dtype, workspace, workspace_bytes, stream))
 
 
-def fa_bwd_rowterm(o, dO, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
-    return int(lib().fa_bwd_rowterm(o, dO, B, H, N, d, dtype, workspace, workspace_bytes, stream))
+def fa_bwd_rowterm(o, dO, lse, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
+    return int(lib().fa_bwd_rowterm(o, dO, lse, B, H, N, d, dtype, workspace, workspace_bytes, stream))
 
 
 def fa_bwd_dkdv(q, k, v, lse, dO, dk, dv, B, H, N, d, scale, mask_kind, block_mask, dtype,
@@ -277,7 +277,8 @@ def backward(q, k, v, o, lse, do, scale=None, mask_kind=MASK_NONE, block_mask=No
                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, mask_kind, mp,
                     dt, workspace.data_ptr(), wsb, stream)
     elif steps == "rowterm":
-        st = fa_bwd_rowterm(o.data_ptr(), do.data_ptr(), B, H, N, d, dt, workspace.data_ptr(), wsb, stream)
+        st = fa_bwd_rowterm(o.data_ptr(), do.data_ptr(), lse.data_ptr(), B, H, N, d, dt, workspace.data_ptr(), wsb,
+                            stream)
     elif steps == "dkdv":
         st = fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
                          dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, mask_kind, mp, dt,

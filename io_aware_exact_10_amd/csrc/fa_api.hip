@@ -94,10 +94,13 @@ const char* fa_status_string(int status) {
   }
 }
 
+// Backward workspace: two float arrays of one entry per query row, each
+// rounded up to 256 bytes: the row term, then the scaled LSE.
+static size_t row_array_bytes(size_t rows) { return (rows * sizeof(float) + 255) & ~(size_t)255; }
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
-  const size_t rows = (size_t)B * (size_t)H * (size_t)N;
-  return (rows * sizeof(float) + 255) & ~(size_t)255;
+  return 2 * row_array_bytes((size_t)B * (size_t)H * (size_t)N);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -177,6 +180,7 @@ int bwd_prepare(const void* q, const void* k, const void* v, const void* o, cons
   p.dk = const_cast<void*>(take(dk));
   p.dv = const_cast<void*>(take(dv));
   p.dterm = (float*)const_cast<void*>(workspace);
+  p.lse2 = (float*)((uint8_t*)const_cast<void*>(workspace) + row_array_bytes((size_t)B * H * N));
   *out = p;
   return FA_OK;
 }
@@ -202,10 +206,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   return st != FA_OK ? st : bwd_launch(p, mask_kind, dtype, fa::kBwdAll, stream);
 }
 
-int fa_bwd_rowterm(const void* o, const void* dO, int B, int H, int N, int d, int dtype,
+int fa_bwd_rowterm(const void* o, const void* dO, const float* lse, int B, int H, int N, int d, int dtype,
                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   fa::AttnParams p;
-  const int st = bwd_prepare(unused, unused, unused, o, (const float*)unused, dO, unused, unused, unused,
+  const int st = bwd_prepare(unused, unused, unused, o, lse, dO, unused, unused, unused,
                              B, H, N, d, 1.0f, FA_MASK_NONE, nullptr, dtype, workspace, workspace_bytes, &p);
   return st != FA_OK ? st : bwd_launch(p, FA_MASK_NONE, dtype, fa::kBwdRowterm, stream);
 }
@@ -288,7 +292,7 @@ extern "C" {
 
 size_t fa_bwd_varlen_workspace_bytes(int total_q, int H, int d) {
   if (total_q < 1 || H < 1 || (d != 64 && d != 128)) return 0;
-  return ((size_t)total_q * (size_t)H * sizeof(float) + 255) & ~(size_t)255;
+  return 2 * row_array_bytes((size_t)total_q * (size_t)H);
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -360,6 +364,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   p.dk = dk;
   p.dv = dv;
   p.dterm = (float*)workspace;
+  p.lse2 = (float*)((uint8_t*)workspace + row_array_bytes((size_t)total_q * H));
   return fa::launch_bwd_bf16(p, mask_kind, fa::kBwdAll, stream) == 0 ? FA_OK : FA_ERR_HIP;
 }
 

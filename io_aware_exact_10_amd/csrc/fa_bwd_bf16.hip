@@ -11,7 +11,11 @@
 //   dQ = scale * dS K           dK = scale * dS^T Q
 //
 // Three kernels, in stream order:
-//   bwd_rowterm   D_i = sum_k dO_ik O_ik (a streaming pass over O and dO).
+//   bwd_rowterm   D_i = sum_k dO_ik O_ik (a streaming pass over O and dO),
+//                 stored negated, and -LSE_i log2(e) (-inf for an empty row),
+//                 so that the loops form P = 2^(c s - LSE log2 e) with one
+//                 FMA and start the dP accumulator at -D (dP - D comes out
+//                 of the product).
 //   bwd_dkdv      one workgroup per 128-key tile (32 keys per wave), looping
 //                 over the visible 64-query tiles: K and V stay in registers
 //                 as MFMA B operands; each Q and dO tile is copied once,
@@ -66,7 +70,10 @@ __global__ __launch_bounds__(kThreads) void bwd_rowterm_bf16_kernel(AttnParams p
   for (int off = DC / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && col == 0) {
     const size_t inner = (size_t)p.rt_inner;
-    p.dterm[(row % inner) * (size_t)p.rt_hs + row / inner] = acc;
+    const size_t idx = (row % inner) * (size_t)p.rt_hs + row / inner;
+    const float l = p.lse[idx];
+    p.dterm[idx] = -acc;
+    p.lse2[idx] = l == -INFINITY ? -INFINITY : -l * kLog2e;
   }
 }
 
@@ -80,8 +87,8 @@ template <int D>
 struct alignas(16) DkvSmem {
   uint8_t q[2][kDkvBQ * D * 2];    // swizzled row-major Q tiles (sign-adjusted on read)
   uint8_t dO[2][kDkvBQ * D * 2];   // swizzled row-major dO tiles
-  float lse[2][kDkvBQ];
-  float dterm[2][kDkvBQ];
+  float lse[2][kDkvBQ];     // -LSE log2(e) of the tile's queries
+  float dterm[2][kDkvBQ];   // -D of the tile's queries
 };
 
 // d = 128 keeps K, V fragments and the dK^T, dV^T accumulators (192 VGPRs)
@@ -113,7 +120,7 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   // Query head hk * G + j: its Q / dO rows and its LSE / row-term entries.
   const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + sq.qb + (int64_t)hk * G * p.q_hs;
   const uint16_t* __restrict__ dOg = (const uint16_t*)p.dO + sq.qb + (int64_t)hk * G * p.q_hs;
-  const float* __restrict__ lseg = p.lse + sq.lb + (int64_t)hk * G * p.l_hs;
+  const float* __restrict__ lseg = p.lse2 + sq.lb + (int64_t)hk * G * p.l_hs;
   const float* __restrict__ dtg = p.dterm + sq.lb + (int64_t)hk * G * p.l_hs;
 
   const int nqt = (Nq + kDkvBQ - 1) / kDkvBQ;
@@ -195,7 +202,15 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
 
     auto sdp = [&](int mb, f32x16& sv, f32x16& dpv) {
       sv = zero16();
-      dpv = zero16();
+      // dP - D: the accumulator starts at -D of each query row.
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 nd = *(const float4*)&sm.dterm[buf][mb * 32 + 8 * g + 4 * h];
+        dpv[4 * g] = nd.x;
+        dpv[4 * g + 1] = nd.y;
+        dpv[4 * g + 2] = nd.z;
+        dpv[4 * g + 3] = nd.w;
+      }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
         sv = mfma_32x32x16(row_frag(sbase + mb * 32 * 2 * D, qr, ks), kf[ks], sv);
@@ -213,19 +228,17 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
           const int g = 2 * st + g2;
           const int ql = mb * 32 + 8 * g + 4 * h;
           const float4 l4 = *(const float4*)&sm.lse[buf][ql];
-          const float4 d4 = *(const float4*)&sm.dterm[buf][ql];
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+          const float nl[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * g + e;
-            float pp = fast_exp2(__builtin_fmaf(sv[i], c, -lv[e] * kLog2e));
+            float pp = fast_exp2(__builtin_fmaf(sv[i], c, nl[e]));
             if (NM) {
               const int q = q0 + ql + e;
               if (q >= Nq || (MASK == 1 && kj > q + off)) pp = 0.f;
             }
             pv[4 * g2 + e] = pp;
-            dv[4 * g2 + e] = pp * (dpv[i] - dd[e]);
+            dv[4 * g2 + e] = pp * dpv[i];
           }
         }
         pb[st] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
@@ -394,12 +407,11 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     qf[ks] = a ^ p.qflip;
     of[ks] = b;
   }
-  float lse2 = INFINITY, dti = 0.f;
+  float nl = -INFINITY, ndt = 0.f;   // -LSE log2(e) and -D of this lane's query
   if (qi < Nq) {
     const int64_t li = sq.lb + hq * p.l_hs + qi;
-    const float l = p.lse[li];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-    dti = p.dterm[li];
+    nl = p.lse2[li];
+    ndt = p.dterm[li];
   }
 
   f32x16 dqT[NDT];
@@ -440,12 +452,12 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * st + e;
-          float pp = fast_exp2(__builtin_fmaf(sv[i], c, -lse2));
+          float pp = fast_exp2(__builtin_fmaf(sv[i], c, nl));
           if (NM) {
             const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
             if (key >= Nk || (MASK == 1 && key > qi + off)) pp = 0.f;
           }
-          y[e] = pp * (dpv[i] - dti);
+          y[e] = pp * (dpv[i] + ndt);
         }
         db[st] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
                        pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};

@@ -17,7 +17,8 @@ struct AttnParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dterm;             // backward row term D [B, H, N] (workspace)
+  float* dterm;             // backward row term (workspace, layout of lse; bf16 path: -D)
+  float* lse2;              // bf16 backward: -LSE * log2(e) (workspace, layout of lse; -inf for empty rows)
   const uint8_t* block_mask;
   int B, H, N, d;
   int nblk;                 // ceil(N / 128): block-mask entries per side

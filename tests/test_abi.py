@@ -76,9 +76,10 @@ def test_status_strings():
 
 
 def test_workspace_bytes():
-    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 64) == 256
-    assert fa.fa_bwd_workspace_bytes(2, 3, 1000, 128) == ((2 * 3 * 1000 * 4 + 255) // 256) * 256
-    assert fa.fa_bwd_workspace_bytes(64, 16, 1024, 64) == 64 * 16 * 1024 * 4
+    """Two float arrays (row term, rescaled LSE), each rounded up to 256 bytes."""
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 64) == 2 * 256
+    assert fa.fa_bwd_workspace_bytes(2, 3, 1000, 128) == 2 * ((2 * 3 * 1000 * 4 + 255) // 256) * 256
+    assert fa.fa_bwd_workspace_bytes(64, 16, 1024, 64) == 2 * 64 * 16 * 1024 * 4
     for bad in ((0, 1, 1, 64), (1, 0, 1, 64), (1, 1, 0, 64), (1, 1, 8, 96)):
         assert fa.fa_bwd_workspace_bytes(*bad) == 0
 
@@ -150,7 +151,7 @@ def test_product_path_does_not_reference_the_oracle():
 def step_args(name, **kw):
     a = bwd_args()
     if name == "rowterm":
-        keep = ["o", "dO", "B", "H", "N", "d", "dtype", "workspace", "workspace_bytes", "stream"]
+        keep = ["o", "dO", "lse", "B", "H", "N", "d", "dtype", "workspace", "workspace_bytes", "stream"]
     elif name == "dkdv":
         keep = ["q", "k", "v", "lse", "dO", "dk", "dv", "B", "H", "N", "d", "scale", "mask_kind",
                 "block_mask", "dtype", "workspace", "workspace_bytes", "stream"]
@@ -183,6 +184,8 @@ def test_bwd_step_validation(name):
         assert f(**step_args(name, lse=4 * BIG + A + 1)) == fa.FA_ERR_ALIGN
     else:
         assert f(**step_args(name, workspace=A + 3 * BIG)) == fa.FA_ERR_ARG   # workspace aliases o
+        assert f(**step_args(name, lse=None)) == fa.FA_ERR_NULL
+        assert f(**step_args(name, workspace=A + 4 * BIG)) == fa.FA_ERR_ARG   # workspace aliases lse
 
 
 # --------------------------------------------------------------------------
@@ -208,8 +211,8 @@ def vbwd_args(**kw):
 
 
 def test_varlen_workspace_bytes():
-    assert fa.fa_bwd_varlen_workspace_bytes(150, 4, 64) == 2560
-    assert fa.fa_bwd_varlen_workspace_bytes(1, 1, 128) == 256
+    assert fa.fa_bwd_varlen_workspace_bytes(150, 4, 64) == 2 * 2560
+    assert fa.fa_bwd_varlen_workspace_bytes(1, 1, 128) == 2 * 256
     for bad in ((0, 1, 64), (1, 0, 64), (5, 2, 32)):
         assert fa.fa_bwd_varlen_workspace_bytes(*bad) == 0
 
