@@ -280,31 +280,36 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
       }
     }
   };
-  auto compute = [&](int buf, int it) {
+  auto needm = [&](int it) {
     const int q0 = it * kDkvBQ;
-    const bool needm = (MASK == 1 && q0 + off < kw0 + 31) || q0 + kDkvBQ > Nq;
-    if (needm)
-      tile(buf, q0, std::true_type{});
-    else
-      tile(buf, q0, std::false_type{});
+    return (MASK == 1 && q0 + off < kw0 + 31) || q0 + kDkvBQ > Nq;
   };
-
-  wait_vmem();
-  __syncthreads();
   int buf = 0;
-  while (it < nqt) {
+  // One pipelined step: issue the copies of the next tile, compute this one.
+  auto step = [&](auto nm) {
     int itn = next_in_head(it + 1), jn = j;
     if (itn >= nqt && j + 1 < G) {   // on to the next query head of the group
       itn = next_in_head(qbeg);
       jn = j + 1;
     }
     if (itn < nqt) issue(itn, jn, buf ^ 1);
-    compute(buf, it);
+    tile(buf, it * kDkvBQ, nm);
     wait_vmem();
     __syncthreads();
     buf ^= 1;
     it = itn;
     j = jn;
+  };
+
+  wait_vmem();
+  __syncthreads();
+  // Masked and unmasked tiles come in runs (the diagonal band, then the
+  // interior, then the ragged tail); each run has a loop of its own, so
+  // the accumulators stay in place instead of being moved where the two
+  // variants of the tile code would join.
+  while (it < nqt) {
+    while (it < nqt && needm(it)) step(std::true_type{});
+    while (it < nqt && !needm(it)) step(std::false_type{});
   }
 
   if (kj < Nk) {
@@ -493,27 +498,34 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
       }
     }
   };
-  auto compute = [&](int buf, int kt) {
+  // Tile classes for this wave: 0 unmasked, 1 masked (diagonal or tail),
+  // 2 wholly past the wave's diagonal (nothing to compute).
+  auto cls = [&](int kt) {
     const int k0 = kt * kDqBK;
-    if (MASK == 1 && k0 > qw0 + 31 + off) return;   // whole tile past this wave's diagonal
-    const bool need_mask = (k0 + kDqBK > Nk) || (MASK == 1 && k0 + kDqBK - 1 > qw0 + off);
-    if (need_mask)
-      tile(buf, kt, std::true_type{});
-    else
-      tile(buf, kt, std::false_type{});
+    if (MASK == 1 && k0 > qw0 + 31 + off) return 2;
+    return ((k0 + kDqBK > Nk) || (MASK == 1 && k0 + kDqBK - 1 > qw0 + off)) ? 1 : 0;
   };
-
-  wait_vmem();
-  __syncthreads();
   int buf = 0;
-  while (kt < kend) {
+  // One pipelined step: issue the copies of the next tile, compute this one.
+  auto step = [&](auto nm, bool work) {
     const int ktn = next_tile(kt + 1);
     if (ktn < kend) issue(ktn, buf ^ 1);
-    compute(buf, kt);
+    if (work) tile(buf, kt, nm);
     wait_vmem();
     __syncthreads();
     buf ^= 1;
     kt = ktn;
+  };
+
+  wait_vmem();
+  __syncthreads();
+  // Each class runs in a loop of its own (runs of equal tiles), so the
+  // accumulators stay in place instead of being moved where the variants of
+  // the tile code would join. Every wave takes one barrier per tile.
+  while (kt < kend) {
+    while (kt < kend && cls(kt) == 0) step(std::false_type{}, true);
+    while (kt < kend && cls(kt) == 1) step(std::true_type{}, true);
+    while (kt < kend && cls(kt) == 2) step(std::false_type{}, false);
   }
 
   if (qi < Nq) {

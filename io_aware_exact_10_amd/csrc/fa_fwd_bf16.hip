@@ -246,14 +246,12 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
       pv(0, pb0);
     }
   };
-  auto compute = [&](int buf, int kt) {
+  // Tile classes for this wave: 0 unmasked, 1 masked (diagonal or tail),
+  // 2 wholly past the wave's diagonal (nothing to compute).
+  auto cls = [&](int kt) {
     const int k0 = kt * kFwdBC;
-    if (MASK == 1 && k0 > qw0 + 31 + off) return;   // whole tile past this wave's diagonal
-    const bool need_mask = (k0 + kFwdBC > Nk) || (MASK == 1 && k0 + kFwdBC - 1 > qw0 + off);
-    if (need_mask)
-      tile(buf, kt, std::true_type{});
-    else
-      tile(buf, kt, std::false_type{});
+    if (MASK == 1 && k0 > qw0 + 31 + off) return 2;
+    return ((k0 + kFwdBC > Nk) || (MASK == 1 && k0 + kFwdBC - 1 > qw0 + off)) ? 1 : 0;
   };
 
   // NBUF - 1 tiles are issued ahead. At the top of an iteration tile kt is
@@ -276,11 +274,11 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   };
   wait_next(NBUF > 2 ? ahead[NBUF > 2 ? NBUF - 3 : 0] : kend);
   int buf = 0;
-  while (kt < kend) {
+  auto step = [&](auto nm, bool work) {
     const int last = NBUF > 2 ? ahead[NBUF > 2 ? NBUF - 3 : 0] : kt;
     const int ktn = last < kend ? next_tile(last + 1) : kend;   // NBUF - 1 tiles after kt
     if (ktn < kend) issue(ktn, (buf + NBUF - 1) % NBUF);
-    compute(buf, kt);
+    if (work) tile(buf, kt, nm);
     wait_next(ktn);
     buf = (buf + 1) % NBUF;
     if (NBUF > 2) {
@@ -291,6 +289,14 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     } else {
       kt = ktn;
     }
+  };
+  // Each class runs in a loop of its own (runs of equal tiles), so the
+  // accumulators stay in place instead of being moved where the variants of
+  // the tile code would join. Every wave takes one barrier per tile.
+  while (kt < kend) {
+    while (kt < kend && cls(kt) == 0) step(std::false_type{}, true);
+    while (kt < kend && cls(kt) == 1) step(std::true_type{}, true);
+    while (kt < kend && cls(kt) == 2) step(std::false_type{}, false);
   }
 
   // Epilogue: combine the two lane halves' partial sums, normalise, store.

@@ -69,11 +69,10 @@ struct alignas(16) F8Smem {
   uint8_t v[2][D * kF8BC];   // V^T tiles, one 64-byte row per d
 };
 
-// NW waves of 32 queries each per workgroup. Three waves per SIMD fit the
-// register budget except for the unmasked d = 128 variant, which the
-// compiler lays out in 256 registers.
+// NW waves of 32 queries each per workgroup; three waves per SIMD fit the
+// register budget.
 template <int D, int MASK, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 128 && MASK == 0 ? 2 : 3)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3)))
 void fwd_fp8_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   constexpr int kF8NW = NW;
   constexpr int kF8BR = 32 * NW;        // queries per workgroup
@@ -239,28 +238,32 @@ void fwd_fp8_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
       acc[dt] = mfma_f8_32x32x64(vf, pb, acc[dt]);
     }
   };
-  auto compute = [&](int buf, int kt) {
+  // Tile classes for this wave: 0 unmasked, 1 masked (diagonal or tail),
+  // 2 wholly past the wave's diagonal. Each class runs in a loop of its own
+  // so the accumulators stay in place (no moves where the variants would
+  // join); every wave takes one barrier per tile.
+  auto cls = [&](int kt) {
     const int k0 = kt * kF8BC;
-    if (MASK == 1 && k0 > qw0 + 31) return;   // whole tile past this wave's diagonal
-    const bool need_mask = (k0 + kF8BC > N) || (MASK == 1 && k0 + kF8BC - 1 > qw0);
-    if (need_mask)
-      tile(buf, kt, std::true_type{});
-    else
-      tile(buf, kt, std::false_type{});
+    if (MASK == 1 && k0 > qw0 + 31) return 2;
+    return ((k0 + kF8BC > N) || (MASK == 1 && k0 + kF8BC - 1 > qw0)) ? 1 : 0;
   };
-
-  wait_vmem();
-  __syncthreads();
   int buf = 0;
-#pragma clang loop unroll(disable)
-  while (kt < kend) {
+  auto step = [&](auto nm, bool work) {
     const int ktn = kt + 1;
     if (ktn < kend) issue(ktn, buf ^ 1);
-    compute(buf, kt);
+    if (work) tile(buf, kt, nm);
     wait_vmem();
     __syncthreads();
     buf ^= 1;
     kt = ktn;
+  };
+
+  wait_vmem();
+  __syncthreads();
+  while (kt < kend) {
+    while (kt < kend && cls(kt) == 0) step(std::false_type{}, true);
+    while (kt < kend && cls(kt) == 1) step(std::true_type{}, true);
+    while (kt < kend && cls(kt) == 2) step(std::false_type{}, false);
   }
 
   const float lt = l_run + __shfl_xor(l_run, 32);

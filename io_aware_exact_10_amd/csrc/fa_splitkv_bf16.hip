@@ -194,7 +194,8 @@ __global__ __launch_bounds__(64 * NW) void splitkv_bf16_kernel(AttnParams p, uin
   };
 
   int buf = 0;
-  for (int kt = kt0; kt < kt1; ++kt) {
+  int kt = kt0;
+  auto step = [&](auto nm) {
     // Tile kt was issued NBUF - 1 tiles ago; later tiles may stay in flight.
     if (kt + NBUF - 2 < kt1 && NBUF > 2)
       wait_vmem_n<(NBUF > 2 ? kPerTile * (NBUF - 2) : 0)>();
@@ -203,14 +204,15 @@ __global__ __launch_bounds__(64 * NW) void splitkv_bf16_kernel(AttnParams p, uin
     __syncthreads();
     const int ktn = kt + NBUF - 1;
     if (ktn < kt1) issue(ktn, (buf + NBUF - 1) % NBUF);
-    const int k0 = kt * BC;
-    const bool need_mask = (k0 + BC > Nk) || (MASK == 1 && k0 + BC - 1 > off);
-    if (need_mask)
-      tile(buf, kt, std::true_type{});
-    else
-      tile(buf, kt, std::false_type{});
+    tile(buf, kt, nm);
     buf = (buf + 1) % NBUF;
-  }
+    ++kt;
+  };
+  // Unmasked tiles come first, masked ones (the causal end, the ragged tail)
+  // last: one loop each, so the accumulators stay in place.
+  auto needm = [&](int t) { return (t * BC + BC > Nk) || (MASK == 1 && t * BC + BC - 1 > off); };
+  while (kt < kt1 && !needm(kt)) step(std::false_type{});
+  while (kt < kt1) step(std::true_type{});
 
   // Partial result of this key range, normalised over the range.
   const float lt = l_run + __shfl_xor(l_run, 32);
