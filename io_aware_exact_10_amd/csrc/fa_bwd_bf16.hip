@@ -200,7 +200,10 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) live[mb] = !NM || !(MASK == 1 && q0 + 32 * mb + 31 + off < kw0);
 
-    auto sdp = [&](int mb, f32x16& sv, f32x16& dpv) {
+    // S and dP of sub-block mb; the sub-block's -LSE log2(e) values are read
+    // from LDS between the two products, so the read latency hides behind the
+    // dP products instead of stalling the exponentials.
+    auto sdp = [&](int mb, f32x16& sv, f32x16& dpv, float nlv[16]) {
       sv = zero16();
       // dP - D: the accumulator starts at -D of each query row.
 #pragma unroll
@@ -215,11 +218,19 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
       for (int ks = 0; ks < D / 16; ++ks)
         sv = mfma_32x32x16(row_frag(sbase + mb * 32 * 2 * D, qr, ks), kf[ks], sv);
 #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = *(const float4*)&sm.lse[buf][mb * 32 + 8 * g + 4 * h];
+        nlv[4 * g] = l4.x;
+        nlv[4 * g + 1] = l4.y;
+        nlv[4 * g + 2] = l4.z;
+        nlv[4 * g + 3] = l4.w;
+      }
+#pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
         dpv = mfma_32x32x16(row_frag(sbase + mb * 32 * 2 * D, orow, ks), vf[ks], dpv);
     };
     // P = 2^(c s - LSE log2 e) and dS = P (dP - D), packed as B operands.
-    auto pds = [&](int mb, const f32x16& sv, const f32x16& dpv, u32x4 pb[2], u32x4 db[2]) {
+    auto pds = [&](int mb, const f32x16& sv, const f32x16& dpv, const float nlv[16], u32x4 pb[2], u32x4 db[2]) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         float pv[8], dv[8];
@@ -227,12 +238,10 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
         for (int g2 = 0; g2 < 2; ++g2) {
           const int g = 2 * st + g2;
           const int ql = mb * 32 + 8 * g + 4 * h;
-          const float4 l4 = *(const float4*)&sm.lse[buf][ql];
-          const float nl[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * g + e;
-            float pp = fast_exp2(__builtin_fmaf(sv[i], c, nl[e]));
+            float pp = fast_exp2(__builtin_fmaf(sv[i], c, nlv[i]));
             if (NM) {
               const int q = q0 + ql + e;
               if (q >= Nq || (MASK == 1 && kj > q + off)) pp = 0.f;
@@ -259,23 +268,24 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     };
 
     f32x16 s0, dp0, s1, dp1;
+    float nl0[16], nl1[16];
     u32x4 pb0[2], db0[2], pb1[2], db1[2];
     if (!NM) {
-      sdp(0, s0, dp0);
+      sdp(0, s0, dp0, nl0);
       __builtin_amdgcn_sched_barrier(0);
-      sdp(1, s1, dp1);
-      pds(0, s0, dp0, pb0, db0);
+      sdp(1, s1, dp1, nl1);
+      pds(0, s0, dp0, nl0, pb0, db0);
       __builtin_amdgcn_sched_barrier(0);
       dkdv(0, pb0, db0);
-      pds(1, s1, dp1, pb1, db1);
+      pds(1, s1, dp1, nl1, pb1, db1);
       __builtin_amdgcn_sched_barrier(0);
       dkdv(1, pb1, db1);
     } else {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         if (!live[mb]) continue;
-        sdp(mb, s0, dp0);
-        pds(mb, s0, dp0, pb0, db0);
+        sdp(mb, s0, dp0, nl0);
+        pds(mb, s0, dp0, nl0, pb0, db0);
         dkdv(mb, pb0, db0);
       }
     }
