@@ -41,8 +41,8 @@ constexpr int kMaskBlock = 128;  // block-sparse mask granularity
 
 // Workgroup shape: NW waves of 32 query rows each, NBUF K/V tiles in LDS
 // (NBUF - 1 copies in flight while one tile is computed). Four waves by
-// default; at d = 128 from 16K queries on, eight waves (256 queries share
-// every K/V tile copied into LDS), 5 % faster at 32K. Double buffering in
+// default; at d = 128 from 16K queries on (8K without a mask), eight waves
+// (256 queries share every K/V tile copied into LDS), 5 % faster at 32K. Double buffering in
 // both: a third buffer was measured slower. Block-sparse keeps four waves so
 // a workgroup's queries stay inside one 128-row mask block.
 template <int D, int MASK, int NW_, int NBUF_>
@@ -318,7 +318,10 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 }
 
 #ifndef FA_FWD_LONG_N
-#define FA_FWD_LONG_N 16384      // query length from which the eight-wave shape is used
+#define FA_FWD_LONG_N 16384      // query length from which the eight-wave shape is used (causal)
+#endif
+#ifndef FA_FWD_LONG_N_FULL
+#define FA_FWD_LONG_N_FULL 8192  // the same without a mask (5 % faster at 8K, measured)
 #endif
 #ifndef FA_FWD_LONG_NBUF
 #define FA_FWD_LONG_NBUF 2
@@ -338,7 +341,8 @@ static int launch_fwd_s(const AttnParams& p, hipStream_t stream) {
 template <int D, int MASK>
 static int launch_fwd_t(const AttnParams& p, hipStream_t stream) {
   if constexpr (MASK != 2 && D == 128) {
-    if (p.Nq >= FA_FWD_LONG_N) return launch_fwd_s<D, MASK, 8, FA_FWD_LONG_NBUF>(p, stream);
+    if (p.Nq >= (MASK == 0 ? FA_FWD_LONG_N_FULL : FA_FWD_LONG_N))
+      return launch_fwd_s<D, MASK, 8, FA_FWD_LONG_NBUF>(p, stream);
   }
   return launch_fwd_s<D, MASK, 4, 2>(p, stream);
 }
