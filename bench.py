@@ -191,6 +191,44 @@ def _pmc_means(db_path: str, counter: str) -> dict:
     return out
 
 
+COUNTER_SET = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+               "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_VALU_TRANS_F32",
+               "SQ_WAVE_CYCLES")
+N_XCD, N_SIMD = 8, 1024
+
+
+def summarize_counters(db_path: str, substrs=("fa::",)) -> str:
+    """Per-kernel means over dispatches of the COUNTER_SET pass, with three
+    derived figures: the shader clock (GRBM_GUI_ACTIVE is summed over the 8
+    XCDs; divided by the dispatch's duration in the same run), the MFMA busy
+    fraction (SQ_VALU_MFMA_BUSY_CYCLES is per SIMD, 1024 SIMDs) and the
+    executed MFMA work (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 FLOPs)."""
+    import collections
+    import sqlite3
+    cur = sqlite3.connect(db_path).cursor()
+    vals = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    dur = collections.defaultdict(dict)
+    for name, did, cn, v, d in cur.execute(
+            "select kernel_name, dispatch_id, counter_name, value, duration from counters_collection"):
+        vals[name][cn][did] += v
+        dur[name][did] = d
+    lines = ["| kernel | dispatches | mean ns | clock GHz | MFMA busy | executed MFMA GFLOP | "
+             + " | ".join(COUNTER_SET) + " |", "|" + "---|" * (6 + len(COUNTER_SET))]
+    for name in sorted(vals):
+        if not any(s in name for s in substrs):
+            continue
+        c = {cn: sum(d.values()) / len(d) for cn, d in vals[name].items()}
+        ns = sum(dur[name].values()) / len(dur[name])
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        ghz = cyc / ns if ns else 0.0
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (N_SIMD * cyc) if cyc else 0.0
+        gflop = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / 1e9
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {len(dur[name])} | {ns:.0f} | {ghz:.2f} | {busy:.3f} | {gflop:.1f} | "
+                     + " | ".join(f"{c.get(cn, float('nan')):.4g}" for cn in COUNTER_SET) + " |")
+    return "\n".join(lines)
+
+
 def summarize_traffic(fetch_db: str, write_db: str, workload: str, copy_bytes: int, update: bool) -> str:
     """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for a copy of copy_bytes."""
@@ -243,8 +281,22 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="fwd and fwd+bwd TFLOP/s over N = 1K..32K (B*N = 32K tokens, H = 16), d = 64/128, "
                          "no mask and causal; one JSON line per point, then a markdown table")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="forward runtime against the query rows per workgroup (32..256) on the GPT-2-medium "
+                         "and causal training shapes, next to the tile-model HBM bytes")
+    ap.add_argument("--summarize-kernel-traffic", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "SUBSTR"),
+                    help="scaled HBM bytes per dispatch of every kernel whose name holds SUBSTR")
+    ap.add_argument("--summarize-counters", metavar="DB",
+                    help="per-kernel table (clock, MFMA busy, executed MFMA FLOPs, ...) from a counter pass")
     args = ap.parse_args()
 
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
+        return 0
+    if args.summarize_kernel_traffic:
+        f_db, w_db, sub = args.summarize_kernel_traffic
+        print(summarize_kernel_traffic(f_db, w_db, args.copy_bytes, sub))
+        return 0
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
         return 0
@@ -268,6 +320,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.sweep:
         return run_sweep(args, dev)
+    if args.tile_sweep:
+        return run_tile_sweep(args, dev)
     if args.workload in synth.PACKED_WORKLOADS:
         return run_packed(args, synth.PACKED_WORKLOADS[args.workload], dev)
     if args.workload in synth.FP8_WORKLOADS:
@@ -599,6 +653,94 @@ def run_sweep(args, dev) -> int:
         print(f"| {r['d']} | {r['mask']} | {r['N']} | {r['B']} | {r['fwd_ms']} | {r['fwd_tflops']} | "
               f"{100 * r['fwd_frac']:.1f} | {r['fwdbwd_ms']} | {r['fwdbwd_tflops']} |")
     return 0
+
+
+TILE_SWEEP_SHAPES = (
+    # name, B, H, N, d, mask kind
+    ("gpt2_medium", 64, 16, 1024, 64, synth.MASK_NONE),
+    ("causal_train", 8, 16, 4096, 128, synth.MASK_CAUSAL),
+)
+TILE_SWEEP_ROWS = (32, 64, 128, 256)
+
+
+def tile_model_bytes(N: int, d: int, rows: int, causal: bool, e: int = 2) -> int:
+    """HBM bytes per head the forward's schedule implies with no cache reuse:
+    Q read and O written once, the LSE written once, and every workgroup of
+    `rows` queries reading the 64-key K and V tiles its rows see."""
+    kv = 0
+    for t in range((N + rows - 1) // rows):
+        keys = min(N, (t + 1) * rows) if causal else N
+        keys = min(N, (keys + 63) // 64 * 64)
+        kv += 2 * keys * d * e
+    return 2 * N * d * e + kv + 4 * N
+
+
+def run_tile_sweep(args, dev) -> int:
+    """Forward runtime against the query rows per workgroup (fa_fwd_tiled,
+    32..256 rows, 64-key tiles) on the GPT-2-medium shape and the causal
+    training shape: HIP-event medians over the timed steps, next to the
+    schedule's own HBM byte count (tile model, no cache reuse)."""
+    import torch
+    import io_aware_exact_10_amd as fa
+
+    gen = torch.Generator(device=dev)
+    rows_out = []
+    for name, B, H, N, d, mask_kind in TILE_SWEEP_SHAPES:
+        gen.manual_seed(5000 + N + d)
+        q, k, v = (torch.randn((B, H, N, d), generator=gen, device=dev, dtype=torch.float32)
+                   .to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(d)
+        vis = N * N if mask_kind == synth.MASK_NONE else N * (N + 1) // 2
+        fl = 4.0 * d * vis * B * H
+        for br in TILE_SWEEP_ROWS:
+            def fwd():
+                fa.forward(q, k, v, scale, mask_kind, None, out=o, lse=lse, block_rows=br)
+
+            for _ in range(args.warmup):
+                fwd()
+            torch.cuda.synchronize()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            for i in range(args.steps):
+                ev[i][0].record()
+                fwd()
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+            model = tile_model_bytes(N, d, br, mask_kind == synth.MASK_CAUSAL) * B * H
+            rec = {"shape": name, "B": B, "H": H, "N": N, "d": d, "mask": "causal" if mask_kind else "none",
+                   "block_rows": br, "fwd_ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                   "tile_model_gb": round(model / 1e9, 3)}
+            rows_out.append(rec)
+            print(json.dumps(rec), flush=True)
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    copy_calibration(args.copy_calibration, dev)
+    print("| shape | rows per workgroup | fwd ms | TFLOP/s | tile-model HBM GB |")
+    print("|---|---|---|---|---|")
+    for r in rows_out:
+        print(f"| {r['shape']} (B={r['B']} H={r['H']} N={r['N']} d={r['d']} {r['mask']}) | {r['block_rows']} | "
+              f"{r['fwd_ms']} | {r['tflops']} | {r['tile_model_gb']} |")
+    return 0
+
+
+def summarize_kernel_traffic(fetch_db: str, write_db: str, copy_bytes: int, substr: str) -> str:
+    """Scaled HBM bytes per dispatch for every kernel whose name holds substr."""
+    fetch = _pmc_means(fetch_db, "FETCH_SIZE")
+    write = _pmc_means(write_db, "WRITE_SIZE")
+    cf = fetch.get(next((n for n in fetch if COPY_KERNEL in n), ""), None)
+    cw = write.get(next((n for n in write if COPY_KERNEL in n), ""), None)
+    if not cf or not cw:
+        raise SystemExit("copy calibration kernel not found in the counter databases")
+    f_scale, w_scale = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    lines = [f"copy of {copy_bytes} B: FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM GB per launch (scaled) |", "|---|---|---|---|"]
+    for n in sorted(fetch):
+        if substr in n and n in write:
+            b = fetch[n] * 1024.0 * f_scale + write[n] * 1024.0 * w_scale
+            lines.append(f"| `{n}` | {fetch[n]:.0f} | {write[n]:.0f} | {b / 1e9:.3f} |")
+    return "\n".join(lines)
 
 
 def run_fp8(args, w: synth.Workload, dev) -> int:

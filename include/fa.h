@@ -66,7 +66,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,        /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,       /* B, H or N < 1, or the element count overflows */
-  FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}, a dtype the call does not take, or too many split-key rows */
+  FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}, a dtype the call does not take, too many split-key rows, or an unknown tile height */
   FA_ERR_MASK = -4,        /* unknown mask_kind, or block_mask NULL for a block-sparse call */
   FA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_ALIGN = -6,       /* a pointer is not aligned as stated above */
@@ -86,6 +86,24 @@ typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale,
            int mask_kind, const uint8_t* block_mask, int dtype, hipStream_t stream);
+
+/*
+ * fa_fwd with the query-tile height chosen by the caller. The block size sets
+ * the HBM traffic: every workgroup of block_rows queries streams the key/value
+ * tiles its rows see, so K/V reads fall as 1 / block_rows while the on-chip
+ * footprint grows ("FlashAttention: exact attention made fast by counting
+ * memory traffic", "The decisive evidence": Fig. 2, runtime against block
+ * size; "The method": Theorem 2). Exists to measure that trade-off; results
+ * equal fa_fwd's up to summation order.
+ *   block_rows  0 (fa_fwd's own choice), or 32, 64, 128 or 256 query rows per
+ *               workgroup (one to eight 64-wide waves; 64 keys per tile).
+ * bf16 only for block_rows != 0. FA_ERR_UNSUPPORTED for another value, for fp32
+ * with block_rows != 0, and for 256 with the block-sparse mask (a workgroup's
+ * queries must stay inside one 128-row mask block). Otherwise as fa_fwd.
+ */
+int fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale,
+                 int mask_kind, const uint8_t* block_mask, int dtype, int block_rows, hipStream_t stream);
 
 /*
  * Bytes of device workspace fa_bwd needs: two float arrays with one entry per

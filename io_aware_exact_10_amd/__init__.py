@@ -28,7 +28,7 @@ __all__ = [
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_MASK",
     "FA_ERR_WORKSPACE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_ARG",
     "MASK_NONE", "MASK_CAUSAL", "MASK_BLOCK_SPARSE", "DTYPE_BF16", "DTYPE_F32",
-    "FAError", "fa_fwd", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
+    "FAError", "fa_fwd", "fa_fwd_tiled", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen", "fa_bwd_varlen",
     "fa_bwd_varlen_workspace_bytes", "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
     "fa_fwd_fp8", "forward", "backward", "forward_varlen", "backward_varlen", "forward_splitkv", "forward_fp8",
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
         L.fa_fwd.restype = i
+        L.fa_fwd_tiled.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, i, vp]
+        L.fa_fwd_tiled.restype = i
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
         L.fa_bwd.restype = i
         L.fa_bwd_rowterm.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
@@ -123,6 +125,11 @@ def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, block_mask, dtype, stream) -> int:
     return int(lib().fa_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), mask_kind,
                             block_mask, dtype, stream))
+
+
+def fa_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, mask_kind, block_mask, dtype, block_rows, stream) -> int:
+    return int(lib().fa_fwd_tiled(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), mask_kind,
+                                  block_mask, dtype, block_rows, stream))
 
 
 def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, mask_kind, block_mask, dtype,
@@ -226,11 +233,13 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def forward(q, k, v, scale=None, mask_kind=MASK_NONE, block_mask=None, out=None, lse=None):
+def forward(q, k, v, scale=None, mask_kind=MASK_NONE, block_mask=None, out=None, lse=None, block_rows=0):
     """Attention forward on the current stream; returns (o, lse).
 
     q, k, v: contiguous [B, H, N, d] bf16 or fp32 GPU tensors; scale defaults
-    to 1/sqrt(d). lse is fp32 [B, H, N] (natural log).
+    to 1/sqrt(d). lse is fp32 [B, H, N] (natural log). ``block_rows`` other
+    than 0 (32, 64, 128, 256; bf16) fixes the query rows per workgroup and
+    calls fa_fwd_tiled.
     """
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
@@ -238,10 +247,14 @@ def forward(q, k, v, scale=None, mask_kind=MASK_NONE, block_mask=None, out=None,
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     mp = _mask_ptr(mask_kind, block_mask, N, q.device)
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                B, H, N, d, scale, mask_kind, mp, _DT[q.dtype], _stream(q.device))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            B, H, N, d, scale, mask_kind, mp, _DT[q.dtype])
+    if block_rows:
+        st, name = fa_fwd_tiled(*args, int(block_rows), _stream(q.device)), "fa_fwd_tiled"
+    else:
+        st, name = fa_fwd(*args, _stream(q.device)), "fa_fwd"
     if st != FA_OK:
-        raise FAError(st, "fa_fwd")
+        raise FAError(st, name)
     return o, lse
 
 

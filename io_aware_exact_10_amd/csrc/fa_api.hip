@@ -84,7 +84,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and the sizes must fit)";
     case FA_ERR_UNSUPPORTED:
       return "unsupported configuration (d must be 64 or 128; dtype as the entry point allows; split-key: "
-             "(H / Hkv) * max_seqlen_q <= 128)";
+             "(H / Hkv) * max_seqlen_q <= 128; tile height 0, 32, 64, 128 or 256, at most 128 with a block-sparse mask)";
     case FA_ERR_MASK: return "invalid mask (unknown mask_kind, or block_mask NULL for block-sparse)";
     case FA_ERR_WORKSPACE: return "workspace NULL or smaller than fa_bwd_workspace_bytes()";
     case FA_ERR_ALIGN: return "misaligned pointer (tensors 16-byte, lse 4-byte aligned)";
@@ -106,10 +106,21 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale,
            int mask_kind, const uint8_t* block_mask, int dtype, hipStream_t stream) {
+  return fa_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, mask_kind, block_mask, dtype, 0, stream);
+}
+
+int fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale,
+                 int mask_kind, const uint8_t* block_mask, int dtype, int block_rows, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int64_t elems = 0;
   int st = check_common(B, H, N, d, scale, mask_kind, block_mask, dtype, &elems);
   if (st != FA_OK) return st;
+  if (block_rows != 0) {
+    const bool known = block_rows == 32 || block_rows == 64 || block_rows == 128 || block_rows == 256;
+    if (!known || dtype != FA_BF16 || (mask_kind == FA_MASK_BLOCK_SPARSE && block_rows > 128))
+      return FA_ERR_UNSUPPORTED;
+  }
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_ALIGN;
   const size_t tb = (size_t)elems * (dtype == FA_BF16 ? 2 : 4);
@@ -123,7 +134,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   p.v = v;
   p.o = o;
   p.lse = lse;
-  const int e = dtype == FA_BF16 ? fa::launch_fwd_bf16(p, mask_kind, stream)
+  const int e = dtype == FA_BF16 ? fa::launch_fwd_bf16(p, mask_kind, stream, block_rows)
                                  : fa::launch_fwd_f32(p, mask_kind, stream);
   return e == 0 ? FA_OK : FA_ERR_HIP;
 }

@@ -7,8 +7,8 @@
 // row log-sum-exp are written; the N x N scores stay in registers.
 //
 // Work decomposition: one workgroup per (query tile, batch, head); each wave
-// owns 32 query rows (8 waves, 256 rows; 4 waves, 128 rows, for the
-// block-sparse mask, whose blocks are 128 rows), and query tiles run
+// owns 32 query rows (4 waves, 128 rows, or 8 waves, 256 rows, for long
+// sequences at d = 128; 32 and 64 rows on request), and query tiles run
 // in parallel over the sequence ("Core ideas": parallelism over the sequence
 // dimension). The workgroup streams 64-key tiles of K and V through LDS,
 // double-buffered: tile t+1 is copied global -> LDS asynchronously (no
@@ -42,9 +42,13 @@ constexpr int kMaskBlock = 128;  // block-sparse mask granularity
 // Workgroup shape: NW waves of 32 query rows each, NBUF K/V tiles in LDS
 // (NBUF - 1 copies in flight while one tile is computed). Four waves by
 // default; at d = 128 from 16K queries on (8K without a mask), eight waves
-// (256 queries share every K/V tile copied into LDS), 5 % faster at 32K. Double buffering in
-// both: a third buffer was measured slower. Block-sparse keeps four waves so
-// a workgroup's queries stay inside one 128-row mask block.
+// (256 queries share every K/V tile copied into LDS), 5 % faster at 32K.
+// Double buffering in both: a third buffer was measured slower. Block-sparse
+// keeps at most four waves so a workgroup's queries stay inside one 128-row
+// mask block. One and two waves (32 and 64 rows) exist for callers that
+// choose the tile height, e.g. to measure K/V traffic against it: every
+// workgroup reads the K/V tiles its rows see, so that traffic scales as
+// 1 / rows per workgroup.
 template <int D, int MASK, int NW_, int NBUF_>
 struct FwdShape {
   static constexpr int NW = NW_;
@@ -102,7 +106,9 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     kend = last < 0 ? 0 : min(nkt, last / kFwdBC + 1);
   }
   MaskScan ms;
-  if (MASK == 2) ms.init(p.block_mask + (size_t)qt * p.nblk, 1, p.nblk);
+  // Mask row of the 128-row block holding this tile (query tiles of at most
+  // 128 rows never straddle two).
+  if (MASK == 2) ms.init(p.block_mask + (size_t)(q0 / kMaskBlock) * p.nblk, 1, p.nblk);
   auto next_tile = [&](int kt) -> int {
     if (MASK != 2 || kt >= kend) return kt < kend ? kt : kend;
     const int blk = kt / TPB;
@@ -339,7 +345,16 @@ static int launch_fwd_s(const AttnParams& p, hipStream_t stream) {
 }
 
 template <int D, int MASK>
-static int launch_fwd_t(const AttnParams& p, hipStream_t stream) {
+static int launch_fwd_t(const AttnParams& p, int block_rows, hipStream_t stream) {
+  switch (block_rows) {
+    case 32: return launch_fwd_s<D, MASK, 1, 2>(p, stream);
+    case 64: return launch_fwd_s<D, MASK, 2, 2>(p, stream);
+    case 128: return launch_fwd_s<D, MASK, 4, 2>(p, stream);
+    case 256:
+      if constexpr (MASK != 2) return launch_fwd_s<D, MASK, 8, FA_FWD_LONG_NBUF>(p, stream);
+      return (int)hipErrorInvalidValue;
+    default: break;
+  }
   if constexpr (MASK != 2 && D == 128) {
     if (p.Nq >= (MASK == 0 ? FA_FWD_LONG_N_FULL : FA_FWD_LONG_N))
       return launch_fwd_s<D, MASK, 8, FA_FWD_LONG_NBUF>(p, stream);
@@ -347,15 +362,15 @@ static int launch_fwd_t(const AttnParams& p, hipStream_t stream) {
   return launch_fwd_s<D, MASK, 4, 2>(p, stream);
 }
 
-int launch_fwd_bf16(const AttnParams& p, int mask_kind, hipStream_t stream) {
+int launch_fwd_bf16(const AttnParams& p, int mask_kind, hipStream_t stream, int block_rows) {
   if (p.d == 64) {
-    if (mask_kind == 0) return launch_fwd_t<64, 0>(p, stream);
-    if (mask_kind == 1) return launch_fwd_t<64, 1>(p, stream);
-    return launch_fwd_t<64, 2>(p, stream);
+    if (mask_kind == 0) return launch_fwd_t<64, 0>(p, block_rows, stream);
+    if (mask_kind == 1) return launch_fwd_t<64, 1>(p, block_rows, stream);
+    return launch_fwd_t<64, 2>(p, block_rows, stream);
   }
-  if (mask_kind == 0) return launch_fwd_t<128, 0>(p, stream);
-  if (mask_kind == 1) return launch_fwd_t<128, 1>(p, stream);
-  return launch_fwd_t<128, 2>(p, stream);
+  if (mask_kind == 0) return launch_fwd_t<128, 0>(p, block_rows, stream);
+  if (mask_kind == 1) return launch_fwd_t<128, 1>(p, block_rows, stream);
+  return launch_fwd_t<128, 2>(p, block_rows, stream);
 }
 
 }  // namespace fa

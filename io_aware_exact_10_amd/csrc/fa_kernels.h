@@ -92,7 +92,9 @@ void set_dense_layout(AttnParams& p);
 // depend only on the row term).
 enum BwdStep { kBwdRowterm = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7 };
 
-int launch_fwd_bf16(const AttnParams& p, int mask_kind, hipStream_t stream);
+// block_rows: query rows per workgroup, 32, 64, 128 or 256 (not 256 with the
+// block-sparse mask); 0 picks by shape.
+int launch_fwd_bf16(const AttnParams& p, int mask_kind, hipStream_t stream, int block_rows = 0);
 int launch_bwd_bf16(const AttnParams& p, int mask_kind, int steps, hipStream_t stream);
 int launch_fwd_f32(const AttnParams& p, int mask_kind, hipStream_t stream);
 // FP8 (E4M3) forward, dense layout, bf16 O.

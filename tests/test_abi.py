@@ -46,7 +46,7 @@ def call_bwd(**kw):
 
 def test_library_exports_every_declared_symbol():
     names = fa.declared_functions()
-    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
+    assert set(names) == {"fa_fwd", "fa_fwd_tiled", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen",
                           "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_splitkv_splits",
                           "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_fp8"}
@@ -109,6 +109,25 @@ def test_bwd_null(name):
 ])
 def test_fwd_validation(kw, code):
     assert call_fwd(**kw) == code
+
+
+def call_fwd_tiled(block_rows, **kw):
+    return fa.fa_fwd_tiled(**fwd_args(**kw), block_rows=block_rows)
+
+
+@pytest.mark.parametrize("block_rows,kw,code", [
+    (16, {}, fa.FA_ERR_UNSUPPORTED), (96, {}, fa.FA_ERR_UNSUPPORTED), (512, {}, fa.FA_ERR_UNSUPPORTED),
+    (-32, {}, fa.FA_ERR_UNSUPPORTED),
+    (64, dict(dtype=fa.DTYPE_F32), fa.FA_ERR_UNSUPPORTED),          # chosen heights are bf16 only
+    (256, dict(mask_kind=2, block_mask=A + 9 * BIG), fa.FA_ERR_UNSUPPORTED),   # straddles mask blocks
+    (64, dict(q=None), fa.FA_ERR_NULL), (64, dict(N=0), fa.FA_ERR_SHAPE),
+    (128, dict(d=96), fa.FA_ERR_UNSUPPORTED), (32, dict(mask_kind=5), fa.FA_ERR_MASK),
+    (64, dict(q=A + 8), fa.FA_ERR_ALIGN), (64, dict(o=A), fa.FA_ERR_ARG),
+    (0, dict(scale=math.nan), fa.FA_ERR_ARG),
+])
+def test_fwd_tiled_validation(block_rows, kw, code):
+    """fa_fwd_tiled checks the tile height on top of fa_fwd's own checks."""
+    assert call_fwd_tiled(block_rows, **kw) == code
 
 
 @pytest.mark.parametrize("kw,code", [
