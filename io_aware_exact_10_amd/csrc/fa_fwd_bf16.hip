@@ -8,7 +8,7 @@
 //
 // Work decomposition: one workgroup per (query tile, batch, head); each wave
 // owns 32 query rows (4 waves, 128 rows, or 8 waves, 256 rows, for long
-// sequences at d = 128; 32 and 64 rows on request), and query tiles run
+// sequences; 32 and 64 rows on request), and query tiles run
 // in parallel over the sequence ("Core ideas": parallelism over the sequence
 // dimension). The workgroup streams 64-key tiles of K and V through LDS,
 // double-buffered: tile t+1 is copied global -> LDS asynchronously (no
@@ -41,8 +41,8 @@ constexpr int kMaskBlock = 128;  // block-sparse mask granularity
 
 // Workgroup shape: NW waves of 32 query rows each, NBUF K/V tiles in LDS
 // (NBUF - 1 copies in flight while one tile is computed). Four waves by
-// default; at d = 128 from 16K queries on (8K without a mask), eight waves
-// (256 queries share every K/V tile copied into LDS), 5 % faster at 32K.
+// default; for long sequences (thresholds at the launch below) eight waves,
+// so 256 queries share every K/V tile copied into LDS.
 // Double buffering in both: a third buffer was measured slower. Block-sparse
 // keeps at most four waves so a workgroup's queries stay inside one 128-row
 // mask block. One and two waves (32 and 64 rows) exist for callers that
@@ -323,11 +323,18 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   }
 }
 
+// Query length from which the eight-wave (256-row) shape is used, from
+// interleaved timings of both shapes at B * N = 32K tokens, H = 16:
+//   causal, d = 128: from 16K (2-4 % faster); causal, d = 64: never (5 % slower at 32K);
+//   no mask, d = 128: from 4K (2 % at 4K, 5-6 % from 8K); no mask, d = 64: from 2K (4-6 %).
 #ifndef FA_FWD_LONG_N
-#define FA_FWD_LONG_N 16384      // query length from which the eight-wave shape is used (causal)
+#define FA_FWD_LONG_N 16384
 #endif
 #ifndef FA_FWD_LONG_N_FULL
-#define FA_FWD_LONG_N_FULL 8192  // the same without a mask (5 % faster at 8K, measured)
+#define FA_FWD_LONG_N_FULL 4096
+#endif
+#ifndef FA_FWD_LONG_N_FULL64
+#define FA_FWD_LONG_N_FULL64 2048
 #endif
 #ifndef FA_FWD_LONG_NBUF
 #define FA_FWD_LONG_NBUF 2
@@ -355,9 +362,12 @@ static int launch_fwd_t(const AttnParams& p, int block_rows, hipStream_t stream)
       return (int)hipErrorInvalidValue;
     default: break;
   }
-  if constexpr (MASK != 2 && D == 128) {
-    if (p.Nq >= (MASK == 0 ? FA_FWD_LONG_N_FULL : FA_FWD_LONG_N))
+  if constexpr (MASK == 0) {
+    if (p.Nq >= (D == 128 ? FA_FWD_LONG_N_FULL : FA_FWD_LONG_N_FULL64))
       return launch_fwd_s<D, MASK, 8, FA_FWD_LONG_NBUF>(p, stream);
+  }
+  if constexpr (MASK == 1 && D == 128) {
+    if (p.Nq >= FA_FWD_LONG_N) return launch_fwd_s<D, MASK, 8, FA_FWD_LONG_NBUF>(p, stream);
   }
   return launch_fwd_s<D, MASK, 4, 2>(p, stream);
 }
