@@ -147,6 +147,20 @@ struct TileLoader {
   }
 };
 
+// Max and sum over the lane pair (l, l ^ 32), the two halves of one query
+// row in the S^T layouts: v_permlane32_swap exchanges the two 32-lane halves
+// in the VALU (no LDS round trip, unlike a shuffle). Given two copies of x,
+// one result holds the low half in both halves and the other the high half,
+// so the max (sum) of the two is the pair's max (sum) in every lane.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N of this wave's vector memory operations are pending.
 template <int N>

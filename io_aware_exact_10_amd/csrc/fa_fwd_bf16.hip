@@ -198,7 +198,7 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
       for (int i = 0; i < 16; ++i) mx1 = fmaxf(mx1, s1[i]);
     }
     float mx = fmaxf(mx0, mx1);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx);
     if (!NM) mx *= c;
     // Raise the reference max only when some row of the wave outgrows it.
     if (__ballot(mx > m_run + kRescaleThreshold)) {
@@ -306,7 +306,7 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   }
 
   // Epilogue: combine the two lane halves' partial sums, normalise, store.
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = xor32_sum(l_run);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (qi < Nq) {
     uint16_t* __restrict__ Orow = (uint16_t*)p.o + sq.qb + hq * p.q_hs + qi * q_rs;

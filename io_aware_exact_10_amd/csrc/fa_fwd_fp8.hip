@@ -188,7 +188,7 @@ void fwd_fp8_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
         }
         mx = fmaxf(mx, t);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx);
     if (!NM) mx *= c;
     if (__ballot(mx > m_run + kF8Rescale)) {
       const float m_new = fmaxf(m_run, mx);
@@ -266,7 +266,7 @@ void fwd_fp8_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     while (kt < kend && cls(kt) == 2) step(std::false_type{}, false);
   }
 
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = xor32_sum(l_run);
   const float inv = lt > 0.f ? p.vscale / lt : 0.f;
   if (qi < N) {
     uint16_t* __restrict__ Orow = (uint16_t*)p.o + (head * N + qi) * D;

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64 * NW) void splitkv_bf16_kernel(AttnParams p, uin
         s[kb][i] = t;
         mx = fmaxf(mx, t);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx);
     if (__ballot(mx > m_run + kSkRescale)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64 * NW) void splitkv_bf16_kernel(AttnParams p, uin
   while (kt < kt1) step(std::true_type{});
 
   // Partial result of this key range, normalised over the range.
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = xor32_sum(l_run);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (live_row) {
     const int64_t tok = sq.lb + qi;
