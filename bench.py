@@ -154,6 +154,29 @@ def naive_step(q, k, v, do, scale, mask_kind, bool_mask, backward):
     return o
 
 
+NAIVE_WHOLE_N = 4096   # longer sequences run the comparator one head at a time (S, P of one head: N^2 elements)
+
+
+def naive_mask(w, mask_t, dev):
+    import torch
+    if w.mask_kind == synth.MASK_CAUSAL:
+        return torch.ones(w.N, w.N, dtype=torch.bool, device=dev).tril()
+    if w.mask_kind == synth.MASK_BLOCK_SPARSE:
+        return mask_t.bool().repeat_interleave(128, 0).repeat_interleave(128, 1)[: w.N, : w.N]
+    return None
+
+
+def naive_full(q, k, v, do, scale, mask_kind, bool_mask, backward):
+    """The comparator over the whole batch, or head by head for long sequences."""
+    if q.shape[2] <= NAIVE_WHOLE_N:
+        return naive_step(q, k, v, do, scale, mask_kind, bool_mask, backward)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            naive_step(q[sl], k[sl], v[sl], do[sl] if backward else None, scale, mask_kind, bool_mask, backward)
+    return None
+
+
 # ---------------------------------------------------------------------------
 # rocprofv3 summaries (text for profiles/), read from the SQLite output
 # ---------------------------------------------------------------------------
@@ -261,6 +284,44 @@ def summarize_traffic(fetch_db: str, write_db: str, workload: str, copy_bytes: i
     return "\n".join(lines)
 
 
+def _pmc_sums(db_path: str, counter: str) -> dict:
+    """Counter totals per kernel name over all its dispatches."""
+    import collections
+    import sqlite3
+    cur = sqlite3.connect(db_path).cursor()
+    tot = collections.defaultdict(float)
+    for name, val in cur.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                                 (counter,)):
+        tot[name] += val
+    return tot
+
+
+def summarize_step_traffic(fetch_db: str, write_db: str, copy_bytes: int, steps: int) -> str:
+    """HBM bytes per step of a run: FETCH_SIZE + WRITE_SIZE summed over every
+    kernel except the device copies and fills, scaled by the calibration copy,
+    divided by the number of steps the run made."""
+    fetch, write = _pmc_sums(fetch_db, "FETCH_SIZE"), _pmc_sums(write_db, "WRITE_SIZE")
+    cf = _pmc_means(fetch_db, "FETCH_SIZE").get(next((n for n in fetch if COPY_KERNEL in n), ""), None)
+    cw = _pmc_means(write_db, "WRITE_SIZE").get(next((n for n in write if COPY_KERNEL in n), ""), None)
+    if not cf or not cw:
+        raise SystemExit("copy calibration kernel not found in the counter databases")
+    f_scale, w_scale = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    # the calibration copy and its source fill; the comparator's mask, built once before the steps
+    skip = (COPY_KERNEL, "__amd_rocclr_fill", "FillFunctor<unsigned char>", "FillFunctor<bool>", "triu_tril")
+    lines = [f"copy of {copy_bytes} B: FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}; {steps} steps",
+             "", "| kernel | FETCH GB per step | WRITE GB per step |", "|---|---|---|"]
+    tf = tw = 0.0
+    for n in sorted(set(fetch) | set(write)):
+        if any(x in n for x in skip):
+            continue
+        fb = fetch.get(n, 0.0) * 1024.0 * f_scale / steps
+        wb = write.get(n, 0.0) * 1024.0 * w_scale / steps
+        tf, tw = tf + fb, tw + wb
+        lines.append(f"| `{n[:120]}` | {fb / 1e9:.3f} | {wb / 1e9:.3f} |")
+    lines += ["", f"Total per step: {tf / 1e9:.2f} GB read + {tw / 1e9:.2f} GB written = {(tf + tw) / 1e9:.2f} GB"]
+    return "\n".join(lines)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,10 +347,18 @@ def main() -> int:
                          "and causal training shapes, next to the tile-model HBM bytes")
     ap.add_argument("--summarize-kernel-traffic", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "SUBSTR"),
                     help="scaled HBM bytes per dispatch of every kernel whose name holds SUBSTR")
+    ap.add_argument("--naive-only", action="store_true",
+                    help="run only the materialise-S comparator, warmup + steps times (for its counter passes)")
+    ap.add_argument("--summarize-step-traffic", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "STEPS"),
+                    help="scaled HBM bytes per step summed over every kernel of a run (copies excluded)")
     ap.add_argument("--summarize-counters", metavar="DB",
                     help="per-kernel table (clock, MFMA busy, executed MFMA FLOPs, ...) from a counter pass")
     args = ap.parse_args()
 
+    if args.summarize_step_traffic:
+        f_db, w_db, steps = args.summarize_step_traffic
+        print(summarize_step_traffic(f_db, w_db, args.copy_bytes, int(steps)))
+        return 0
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
         return 0
@@ -351,6 +420,19 @@ def main() -> int:
         if backward:
             fa.backward(q, k, v, o, lse, do, w.scale, w.mask_kind, mask_t, workspace=ws, dq=dq, dk=dk, dv=dv)
 
+    if args.naive_only:
+        # Only the comparator, warmup + steps times (for a counter pass over its kernels).
+        bm = naive_mask(w, mask_t, dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.warmup + args.steps):
+            naive_full(q, k, v, do, w.scale, w.mask_kind, bm, backward)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / max(1, args.warmup + args.steps)
+        copy_calibration(args.copy_calibration, dev)
+        print(json.dumps({"naive_only": w.name, "steps": args.warmup + args.steps, "wall_ms_per_step": round(ms, 3)}))
+        return 0
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -392,42 +474,41 @@ def main() -> int:
 
     peak = PEAK_BF16_TFLOPS if w.dtype == synth.DTYPE_BF16 else PEAK_F32_VALU_TFLOPS
     kflop = {"fwd": fwd_flop, "rowterm": 0.0, "dkdv": 8.0 * w.d * vis * heads, "dq": 2.0 * w.d * vis * heads}
+    kname = KERNEL_NAMES if w.dtype == synth.DTYPE_BF16 else {n: KERNEL_NAMES[n].replace("_bf16_", "_f32_")
+                                                              for n in names}
     kernels = {}
     for n in names:
         t = float(per[n].mean())
-        kernels[n] = {"kernel": KERNEL_NAMES[n], "mean_ms": round(t, 4), "algorithmic_gflop": round(kflop[n] / 1e9, 2),
+        kernels[n] = {"kernel": kname[n], "mean_ms": round(t, 4), "algorithmic_gflop": round(kflop[n] / 1e9, 2),
                       "tflops": round(kflop[n] / (t * 1e-3) / 1e12, 2)}
     dom = max((n for n in names if n != "rowterm"), key=lambda n: per[n].mean())
     dom_t = float(per[dom].mean())
     achieved = kflop[dom] / (dom_t * 1e-3) / 1e12
     traffic = measured_traffic(w.name, dom)
-    roofline = {"kernel": KERNEL_NAMES[dom],
+    roofline = {"kernel": kname[dom],
                 "bound": "mfma" if w.dtype == synth.DTYPE_BF16 else "alu",
                 "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "flop_per_launch": kflop[dom], "mean_launch_ms": round(dom_t, 4)}
 
     naive = None
-    if not args.no_naive and w.N <= 4096:
+    if not args.no_naive:
         try:
-            bm = None
-            if w.mask_kind == synth.MASK_CAUSAL:
-                bm = torch.ones(w.N, w.N, dtype=torch.bool, device=dev).tril()
-            elif w.mask_kind == synth.MASK_BLOCK_SPARSE:
-                bm = mask_t.bool().repeat_interleave(128, 0).repeat_interleave(128, 1)[: w.N, : w.N]
+            bm = naive_mask(w, mask_t, dev)
             for _ in range(2):
-                naive_step(q, k, v, do, w.scale, w.mask_kind, bm, backward)
+                naive_full(q, k, v, do, w.scale, w.mask_kind, bm, backward)
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = 3
             e0.record(stream)
             for _ in range(reps):
-                naive_step(q, k, v, do, w.scale, w.mask_kind, bm, backward)
+                naive_full(q, k, v, do, w.scale, w.mask_kind, bm, backward)
             e1.record(stream)
             torch.cuda.synchronize()
             nms = e0.elapsed_time(e1) / reps
             naive = {"ms_per_step": round(nms, 3), "tflops": round((fwd_flop + bwd_flop) / (nms * 1e-3) / 1e12, 2),
-                     "what": "torch matmul, mask, softmax (fp32), matmul; autograd backward"}
+                     "what": "torch matmul, mask, softmax (fp32), matmul; autograd backward"
+                             + ("; one head at a time" if w.N > NAIVE_WHOLE_N else "")}
         except Exception as ex:  # noqa: BLE001
             naive = {"error": repr(ex)[:200]}
         torch.cuda.empty_cache()
