@@ -100,7 +100,11 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   constexpr int NDT = D / 32;
   constexpr int QPB = kMaskBlk / kDkvBQ;               // query tiles per mask block
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The wave index is the same in every lane; reading it into a scalar makes
+  // everything derived from it (row ranges, tile classes, loop bounds, LDS
+  // copy destinations) scalar, so the tile loops branch on scalars instead of
+  // exec masks.
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
   const uint32_t L = xcd_remap(blockIdx.x, total);
   const uint32_t bh = L / nkt;                 // (K/V head, batch), head-major as in the forward kernel
@@ -364,7 +368,11 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   constexpr int NDT = D / 32;
   constexpr int TPB = kMaskBlk / kDqBK;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The wave index is the same in every lane; reading it into a scalar makes
+  // everything derived from it (row ranges, tile classes, loop bounds, LDS
+  // copy destinations) scalar, so the tile loops branch on scalars instead of
+  // exec masks.
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
   const uint32_t L = xcd_remap(blockIdx.x, total);
   const uint32_t bh = L / nqt;

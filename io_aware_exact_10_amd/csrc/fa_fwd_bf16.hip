@@ -75,7 +75,14 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   constexpr int TPB = kMaskBlock / kFwdBC;                 // key tiles per mask block
   constexpr int NDT = D / 32;                              // 32-row blocks of O^T
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The wave index is the same in every lane; reading it into a scalar makes
+  // everything derived from it (row ranges, tile classes, loop bounds, LDS
+  // copy destinations) scalar, so the tile loops branch on scalars instead of
+  // exec masks. Measured faster for every shape except the causal eight-wave
+  // one (3 % slower there), which keeps the vector form.
+  constexpr bool kScalarWave = !(MASK == 1 && NW_ == 8);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = kScalarWave ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int h = lane >> 5, r = lane & 31;
 
   const uint32_t L = xcd_remap(blockIdx.x, total);

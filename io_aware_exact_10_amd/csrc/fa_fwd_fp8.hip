@@ -83,7 +83,11 @@ void fwd_fp8_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   constexpr int PER = PK / kF8NW;        // pieces per wave
   static_assert(PK % kF8NW == 0, "pieces per wave");
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The wave index is the same in every lane; reading it into a scalar makes
+  // everything derived from it (row ranges, tile classes, loop bounds, LDS
+  // copy destinations) scalar, so the tile loops branch on scalars instead of
+  // exec masks.
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
   const uint32_t L = xcd_remap(blockIdx.x, total);
   const uint32_t bh = L / nqt;

@@ -61,7 +61,11 @@ __global__ __launch_bounds__(64 * NW) void splitkv_bf16_kernel(AttnParams p, uin
   using Loader = TileLoader<D, BC, NW>;
   constexpr int kPerTile = 2 * Loader::PER;   // this wave's copy instructions per K+V tile
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The wave index is the same in every lane; reading it into a scalar makes
+  // everything derived from it (row ranges, tile classes, loop bounds, LDS
+  // copy destinations) scalar, so the tile loops branch on scalars instead of
+  // exec masks.
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
   const int S = p.splits;
   const uint32_t L = xcd_remap(blockIdx.x, total);
