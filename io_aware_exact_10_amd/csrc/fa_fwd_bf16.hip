@@ -78,11 +78,8 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   // The wave index is the same in every lane; reading it into a scalar makes
   // everything derived from it (row ranges, tile classes, loop bounds, LDS
   // copy destinations) scalar, so the tile loops branch on scalars instead of
-  // exec masks. Measured faster for every shape except the causal eight-wave
-  // one (3 % slower there), which keeps the vector form.
-  constexpr bool kScalarWave = !(MASK == 1 && NW_ == 8);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = kScalarWave ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
+  // exec masks.
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
 
   const uint32_t L = xcd_remap(blockIdx.x, total);
@@ -170,7 +167,8 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     int kbase = kbase_l + (int)(sm.k[buf] - sbase);
     int vbase0 = vbase0_l + (int)(sm.v[buf] - sbase), vbase1 = vbase1_l + (int)(sm.v[buf] - sbase);
     asm volatile("" : "+v"(kbase), "+v"(vbase0), "+v"(vbase1));
-    const bool live1 = !(MASK == 1 && k0 + 32 > qw0 + 31 + off);
+    // Unmasked tiles are visible to every row, so both sub-blocks are live.
+    const bool live1 = !NM || !(MASK == 1 && k0 + 32 > qw0 + 31 + off);
 
     u32x4 kf[D / 16];
 #pragma unroll
