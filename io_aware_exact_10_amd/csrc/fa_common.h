@@ -48,23 +48,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
-
-// Low and high bf16 halves of two dwords, interleaved: {a.lo, b.lo} / {a.hi, b.hi}.
-__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Sum of the two bf16 halves of a packed pair, accumulated into c (fp32).
-__device__ __forceinline__ float dot2_ones(uint32_t pair, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
-                                        __builtin_bit_cast(bf16x2, 0x3f803f80u), c, false);
-}
 
 // ---------------------------------------------------------------------------
 // LDS tiles: dense row-major [rows][D] bf16, 16-byte chunk c of row r stored
@@ -201,24 +186,6 @@ __device__ __forceinline__ u32x4 col_frag(const uint8_t* tile_row0, int base0, i
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_row0 + (base1 ^ (64 * dt))));
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
-}
-
-// A chain of NOPS MFMAs whose A fragments come from LDS, with the fragment
-// reads issued LA operations ahead of their use so LDS latency overlaps the
-// preceding MFMAs: load(i) returns fragment i, op(i, frag) issues MFMA i.
-template <int NOPS, int LA, class LoadF, class OpF>
-__device__ __forceinline__ void lds_pipelined(LoadF&& load, OpF&& op) {
-  static_assert(LA >= 1, "lookahead");
-  constexpr int L = LA < NOPS ? LA : NOPS;
-  u32x4 fr[L];
-#pragma unroll
-  for (int j = 0; j < L; ++j) fr[j] = load(j);
-#pragma unroll
-  for (int i = 0; i < NOPS; ++i) {
-    const u32x4 cur = fr[i % L];
-    if (i + L < NOPS) fr[i % L] = load(i + L);
-    op(i, cur);
-  }
 }
 
 // Workgroup id -> logical tile id so that consecutive logical tiles (the query

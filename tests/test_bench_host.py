@@ -1,0 +1,83 @@
+"""Host-side logic of bench.py (CPU only): the FLOP accounting against the
+oracle's own visibility definition, the tile-model byte count against its
+closed forms, and the counter summaries on small synthetic databases."""
+import math
+import sqlite3
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import synth
+
+
+@pytest.mark.parametrize("mask_kind", [synth.MASK_NONE, synth.MASK_CAUSAL, synth.MASK_BLOCK_SPARSE])
+@pytest.mark.parametrize("N", [1, 100, 128, 300, 513])
+def test_visible_pairs_match_oracle_mask(N, mask_kind):
+    """The benchmark's FLOP count uses exactly the pairs the oracle treats as visible."""
+    w = synth.small_workload(1, 1, N, 64, synth.DTYPE_BF16, mask_kind, seed=11 + N)
+    inp = synth.make_inputs(w)
+    vis = oracle.visible(np.arange(N), N, mask_kind, inp.mask)
+    assert bench.visible_pairs(w, inp.mask) == int(vis.sum())
+
+
+@pytest.mark.parametrize("rows", [32, 64, 128, 256])
+@pytest.mark.parametrize("N,d", [(1024, 64), (4096, 128), (640, 128)])
+def test_tile_model_closed_forms(N, d, rows):
+    e = 2
+    nt = math.ceil(N / rows)
+    full = 2 * N * d * e + nt * 2 * N * d * e + 4 * N
+    assert bench.tile_model_bytes(N, d, rows, False) == full
+    # causal, N a multiple of 64: query tile t reads the keys up to its last row, in 64-key tiles
+    causal = 2 * N * d * e + 4 * N + sum(2 * min(N, math.ceil(min(N, (t + 1) * rows) / 64) * 64) * d * e
+                                         for t in range(nt))
+    assert bench.tile_model_bytes(N, d, rows, True) == causal
+    assert bench.tile_model_bytes(N, d, rows, True) < full or nt == 1
+
+
+def test_tile_model_falls_with_height():
+    vals = [bench.tile_model_bytes(4096, 128, r, True) for r in (32, 64, 128, 256)]
+    assert all(a > b for a, b in zip(vals, vals[1:]))
+
+
+def _db(path, rows):
+    con = sqlite3.connect(path)
+    con.execute("create table counters_collection (kernel_name text, dispatch_id int, counter_name text,"
+                " value real, duration real)")
+    con.executemany("insert into counters_collection values (?, ?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+
+
+def test_traffic_summaries_scale_by_the_copy(tmp_path):
+    """FETCH_SIZE / WRITE_SIZE (KiB) are scaled so that the calibration copy
+    reads and writes exactly its own size; per-launch means and per-step sums."""
+    copy = 1 << 30
+    f, w = str(tmp_path / "f.db"), str(tmp_path / "w.db")
+    k = "void fa::fwd_bf16_kernel<64, 0, 4, 2>(fa::AttnParams, unsigned int, unsigned int)"
+    # the copy reads 2x its size by this counter and writes 1x; the kernel: two dispatches
+    _db(f, [(bench.COPY_KERNEL, 1, "FETCH_SIZE", copy / 1024 * 2, 1.0),
+            (k, 2, "FETCH_SIZE", 1000.0, 1.0), (k, 3, "FETCH_SIZE", 3000.0, 1.0)])
+    _db(w, [(bench.COPY_KERNEL, 1, "WRITE_SIZE", copy / 1024, 1.0),
+            (k, 2, "WRITE_SIZE", 500.0, 1.0), (k, 3, "WRITE_SIZE", 500.0, 1.0)])
+    out = bench.summarize_kernel_traffic(f, w, copy, "fwd_bf16")
+    row = [l for l in out.splitlines() if "fwd_bf16_kernel" in l][0]
+    per_launch = (2000.0 * 1024 / 2 + 500.0 * 1024) / 1e9        # mean FETCH halved, WRITE as is
+    assert float(row.split("|")[-2]) == pytest.approx(per_launch, abs=1e-3)
+    step = bench.summarize_step_traffic(f, w, copy, 2)
+    total = [l for l in step.splitlines() if l.startswith("Total per step")][0]
+    assert f"{(4000.0 * 1024 / 2) / 2 / 1e9:.2f} GB read" in total
+    assert f"{1000.0 * 1024 / 2 / 1e9:.2f} GB written" in total
+
+
+def test_counter_summary_derived_columns(tmp_path):
+    db = str(tmp_path / "c.db")
+    k = "void fa::bwd_dq_bf16_kernel<128, 1>(fa::AttnParams, unsigned int, unsigned int)"
+    cyc, ns = 1.9e6, 1.0e6                       # 1.9 GHz over 1 ms
+    rows = [(k, 1, "GRBM_GUI_ACTIVE", cyc * 8, ns), (k, 1, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1024 * cyc, ns),
+            (k, 1, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e9, ns)]
+    _db(db, rows)
+    line = [l for l in bench.summarize_counters(db).splitlines() if "bwd_dq" in l][0]
+    cells = [c.strip() for c in line.split("|")]
+    assert cells[4] == "1.90" and cells[5] == "0.500" and cells[6] == "512.0"
