@@ -284,6 +284,46 @@ def summarize_traffic(fetch_db: str, write_db: str, workload: str, copy_bytes: i
     return "\n".join(lines)
 
 
+STALL_SET_A = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+               "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS")
+STALL_SET_B = ("SQ_ACTIVE_INST_MISC", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+               "SQ_INSTS_SALU", "SQ_ACTIVE_INST_VALU2", "SQ_INSTS_MFMA")
+
+
+def summarize_stalls(db_paths, substrs=("fa::",)) -> str:
+    """Where each kernel's waves spend their cycles, from the STALL_SET_A
+    pass (and optionally STALL_SET_B): the shares of SQ_WAVE_CYCLES spent
+    issuing (SQ_ACTIVE_INST_ANY), waiting on a dependency such as s_waitcnt
+    or a barrier (SQ_WAIT_ANY) and ready but not issued (SQ_WAIT_INST_ANY);
+    the three partition a wave's life. Also the vector and LDS issue shares
+    and, with the second pass, instructions per MFMA."""
+    import collections
+    import sqlite3
+    vals = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    for db in db_paths:
+        cur = sqlite3.connect(db).cursor()
+        for name, did, cn, v in cur.execute(
+                "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+            vals[name][cn][did] += v
+    lines = ["| kernel | issuing | waiting on a dependency | waiting for issue | VALU active | LDS active | "
+             "VALU instr. per MFMA | LDS instr. per MFMA |", "|---|---|---|---|---|---|---|---|"]
+    for name in sorted(vals):
+        if not any(x in name for x in substrs):
+            continue
+        c = {cn: sum(d.values()) / len(d) for cn, d in vals[name].items()}
+        wc = c.get("SQ_WAVE_CYCLES", 0.0)
+        if not wc:
+            continue
+        share = lambda k: f"{100.0 * c[k] / wc:.1f} %" if k in c else "—"
+        mf = c.get("SQ_INSTS_MFMA", 0.0)
+        per = lambda k: f"{c[k] / mf:.2f}" if mf and k in c else "—"
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {share('SQ_ACTIVE_INST_ANY')} | {share('SQ_WAIT_ANY')} | "
+                     f"{share('SQ_WAIT_INST_ANY')} | {share('SQ_ACTIVE_INST_VALU')} | {share('SQ_ACTIVE_INST_LDS')} | "
+                     f"{per('SQ_INSTS_VALU')} | {per('SQ_INSTS_LDS')} |")
+    return "\n".join(lines)
+
+
 def _pmc_sums(db_path: str, counter: str) -> dict:
     """Counter totals per kernel name over all its dispatches."""
     import collections
@@ -351,6 +391,9 @@ def main() -> int:
                     help="run only the materialise-S comparator, warmup + steps times (for its counter passes)")
     ap.add_argument("--summarize-step-traffic", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "STEPS"),
                     help="scaled HBM bytes per step summed over every kernel of a run (copies excluded)")
+    ap.add_argument("--summarize-stalls", nargs="+", metavar="DB",
+                    help="per-kernel shares of wave cycles (issuing / waiting on a dependency / waiting for issue) "
+                         "from the stall counter passes")
     ap.add_argument("--summarize-counters", metavar="DB",
                     help="per-kernel table (clock, MFMA busy, executed MFMA FLOPs, ...) from a counter pass")
     args = ap.parse_args()
@@ -361,6 +404,9 @@ def main() -> int:
         return 0
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
+        return 0
+    if args.summarize_stalls:
+        print(summarize_stalls(args.summarize_stalls))
         return 0
     if args.summarize_kernel_traffic:
         f_db, w_db, sub = args.summarize_kernel_traffic

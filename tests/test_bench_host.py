@@ -81,3 +81,17 @@ def test_counter_summary_derived_columns(tmp_path):
     line = [l for l in bench.summarize_counters(db).splitlines() if "bwd_dq" in l][0]
     cells = [c.strip() for c in line.split("|")]
     assert cells[4] == "1.90" and cells[5] == "0.500" and cells[6] == "512.0"
+
+
+def test_stall_summary_shares(tmp_path):
+    """Shares of SQ_WAVE_CYCLES from two counter passes, and instructions per MFMA."""
+    a, b = str(tmp_path / "a.db"), str(tmp_path / "b.db")
+    k = "void fa::fwd_bf16_kernel<128, 1, 8, 2>(fa::AttnParams, unsigned int, unsigned int)"
+    _db(a, [(k, 1, "SQ_WAVE_CYCLES", 1000.0, 1.0), (k, 1, "SQ_ACTIVE_INST_ANY", 350.0, 1.0),
+            (k, 1, "SQ_WAIT_ANY", 400.0, 1.0), (k, 1, "SQ_WAIT_INST_ANY", 250.0, 1.0),
+            (k, 1, "SQ_ACTIVE_INST_VALU", 200.0, 1.0)])
+    _db(b, [(k, 1, "SQ_INSTS_MFMA", 10.0, 1.0), (k, 1, "SQ_INSTS_VALU", 55.0, 1.0), (k, 1, "SQ_INSTS_LDS", 15.0, 1.0)])
+    line = [l for l in bench.summarize_stalls([a, b]).splitlines() if "fwd_bf16" in l][0]
+    cells = [c.strip() for c in line.split("|")]
+    assert cells[2:7] == ["35.0 %", "40.0 %", "25.0 %", "20.0 %", "—"]
+    assert cells[7:9] == ["5.50", "1.50"]
