@@ -71,6 +71,12 @@ def measured_traffic(workload: str, key: str):
     return None
 
 
+def hbm_rate(traffic, ms):
+    """Achieved HBM GB/s of a launch: measured bytes per launch over its mean
+    duration (None when the bytes are not measured for this kernel source)."""
+    return None if traffic is None or not ms else round(traffic / (ms * 1e-3) / 1e9, 1)
+
+
 def copy_calibration(nbytes: int, dev) -> None:
     """One device-to-device copy of nbytes: the reference dispatch the
     FETCH_SIZE / WRITE_SIZE counters are scaled by."""
@@ -526,7 +532,8 @@ def main() -> int:
     for n in names:
         t = float(per[n].mean())
         kernels[n] = {"kernel": kname[n], "mean_ms": round(t, 4), "algorithmic_gflop": round(kflop[n] / 1e9, 2),
-                      "tflops": round(kflop[n] / (t * 1e-3) / 1e12, 2)}
+                      "tflops": round(kflop[n] / (t * 1e-3) / 1e12, 2),
+                      "hbm_gbs": hbm_rate(measured_traffic(w.name, n), t)}
     dom = max((n for n in names if n != "rowterm"), key=lambda n: per[n].mean())
     dom_t = float(per[dom].mean())
     achieved = kflop[dom] / (dom_t * 1e-3) / 1e12
@@ -534,7 +541,7 @@ def main() -> int:
     roofline = {"kernel": kname[dom],
                 "bound": "mfma" if w.dtype == synth.DTYPE_BF16 else "alu",
                 "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "traffic_gbs": hbm_rate(traffic, dom_t),
                 "flop_per_launch": kflop[dom], "mean_launch_ms": round(dom_t, 4)}
 
     naive = None
@@ -712,8 +719,9 @@ def run_packed(args, w: synth.PackedWorkload, dev) -> int:
                 if w.backward else None),
         "roofline": {"kernel": KERNEL_NAMES["fwd"], "bound": "mfma", "achieved": round(fwd_tf, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name, "fwd"), "flop_per_launch": fwd_flop,
-                     "mean_launch_ms": round(float(fwd_ms.mean()), 4)},
+                     "traffic": measured_traffic(w.name, "fwd"),
+                     "traffic_gbs": hbm_rate(measured_traffic(w.name, "fwd"), float(fwd_ms.mean())),
+                     "flop_per_launch": fwd_flop, "mean_launch_ms": round(float(fwd_ms.mean()), 4)},
         "cpu_baseline": cpu,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }
@@ -940,8 +948,9 @@ def run_fp8(args, w: synth.Workload, dev) -> int:
         "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
         "roofline": {"kernel": "fwd_fp8_kernel", "bound": "mfma", "achieved": round(tf, 2),
                      "peak": round(PEAK_FP8_TFLOPS, 1), "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name, "fwd_fp8"), "flop_per_launch": flop,
-                     "mean_launch_ms": round(ms, 4)},
+                     "traffic": measured_traffic(w.name, "fwd_fp8"),
+                     "traffic_gbs": hbm_rate(measured_traffic(w.name, "fwd_fp8"), ms),
+                     "flop_per_launch": flop, "mean_launch_ms": round(ms, 4)},
         "cpu_baseline": cpu,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }

@@ -95,3 +95,9 @@ def test_stall_summary_shares(tmp_path):
     cells = [c.strip() for c in line.split("|")]
     assert cells[2:7] == ["35.0 %", "40.0 %", "25.0 %", "20.0 %", "—"]
     assert cells[7:9] == ["5.50", "1.50"]
+
+
+def test_hbm_rate():
+    assert bench.hbm_rate(None, 1.0) is None
+    assert bench.hbm_rate(8e9, 1.0) == 8000.0            # 8 GB in 1 ms
+    assert bench.hbm_rate(541e6, 0.3445) == round(541e6 / 0.3445e-3 / 1e9, 1)
