@@ -202,6 +202,40 @@ def fa_fwd_fp8(q, k, v_t, o, lse, B, H, N, d, ldv, scale, q_descale, k_descale, 
 _DT = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}
 
 
+def _need(t, name, shape, dtype):
+    """Structure of one tensor argument (shape, dtype, contiguity); the
+    device is checked separately (``_on_gpu``) after every structural check,
+    so a wrong shape is reported whatever device the tensors are on."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_workspace(t, need):
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+        raise ValueError("workspace must be a contiguous torch tensor")
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes, got {t.numel() * t.element_size()}")
+
+
+def _on_gpu(device, **tensors):
+    """Every tensor argument lives on the GPU that holds q (the kernels take
+    raw pointers, so a tensor elsewhere would be read or written out of its
+    allocation)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name}: tensors must be on the GPU")
+        if t.device != device:
+            raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
 def _check_qkv(q, k, v):
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
@@ -209,11 +243,9 @@ def _check_qkv(q, k, v):
         raise ValueError("q, k, v must have the same shape")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT:
         raise ValueError("q, k, v must all be bfloat16 or all float32")
-    for t in (q, k, v):
-        if not t.is_cuda:
-            raise ValueError("tensors must be on the GPU")
+    for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+            raise ValueError(f"{name}: tensors must be contiguous")
 
 
 def _mask_ptr(mask_kind, block_mask, N, device):
@@ -244,6 +276,11 @@ def forward(q, k, v, scale=None, mask_kind=MASK_NONE, block_mask=None, out=None,
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is not None:
+        _need(out, "out", q.shape, q.dtype)
+    if lse is not None:
+        _need(lse, "lse", (B, H, N), torch.float32)
+    _on_gpu(q.device, q=q, k=k, v=v, out=out, lse=lse)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     mp = _mask_ptr(mask_kind, block_mask, N, q.device)
@@ -269,13 +306,17 @@ def backward(q, k, v, o, lse, do, scale=None, mask_kind=MASK_NONE, block_mask=No
     """
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
-    for t in (o, do):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("o and do must match q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    _need(o, "o", q.shape, q.dtype)
+    _need(do, "do", q.shape, q.dtype)
+    _need(lse, "lse", (B, H, N), torch.float32)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None:
+            _need(t, name, q.shape, q.dtype)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is not None:
+        _need_workspace(workspace, need)
+    _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv, workspace=workspace)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q) if dq is None else dq
@@ -311,12 +352,12 @@ def _check_varlen(q, k, v, cu_q, cu_k):
         raise ValueError("q must be [total_q, H, d]; k and v [total_k, Hkv, d]")
     if k.shape != v.shape or q.shape[2] != k.shape[2]:
         raise ValueError("k and v must match, and share d with q")
-    for t in (q, k, v):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous bfloat16 GPU tensors")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name}: q, k, v must be contiguous bfloat16 tensors")
     for c in (cu_q, cu_k):
-        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_cuda or not c.is_contiguous():
-            raise ValueError("cu_seqlens must be contiguous int32 GPU tensors")
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32 tensors")
     if cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
 
@@ -334,6 +375,11 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
     Tk, Hkv = k.shape[:2]
     B = cu_seqlens_q.numel() - 1
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is not None:
+        _need(out, "out", q.shape, q.dtype)
+    if lse is not None:
+        _need(lse, "lse", (H, Tq), torch.float32)
+    _on_gpu(q.device, q=q, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, out=out, lse=lse)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
     st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -351,14 +397,20 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     Tq, H, d = q.shape
     Tk, Hkv = k.shape[:2]
     B = cu_seqlens_q.numel() - 1
-    for t in (o, do):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("o and do must match q")
-    if lse.shape != (H, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [H, total_q]")
+    _need(o, "o", q.shape, q.dtype)
+    _need(do, "do", q.shape, q.dtype)
+    _need(lse, "lse", (H, Tq), torch.float32)
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is not None:
+            _need(t, name, ref.shape, ref.dtype)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = fa_bwd_varlen_workspace_bytes(Tq, H, d)
+    if workspace is not None:
+        _need_workspace(workspace, need)
+    _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse, do=do, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+            dq=dq, dk=dk, dv=dv, workspace=workspace)
     if workspace is None:
-        workspace = torch.empty(fa_bwd_varlen_workspace_bytes(Tq, H, d), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -385,8 +437,17 @@ def forward_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     splits = fa_splitkv_splits(B, Hkv, int(max_seqlen_k), int(num_splits))
     if splits < 0:
         raise FAError(splits, "fa_splitkv_splits")
+    need = fa_splitkv_workspace_bytes(Tq, H, d, splits)
+    if out is not None:
+        _need(out, "out", q.shape, q.dtype)
+    if lse is not None:
+        _need(lse, "lse", (H, Tq), torch.float32)
+    if workspace is not None:
+        _need_workspace(workspace, need)
+    _on_gpu(q.device, q=q, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, out=out, lse=lse,
+            workspace=workspace)
     if workspace is None:
-        workspace = torch.empty(fa_splitkv_workspace_bytes(Tq, H, d, splits), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
     st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -406,8 +467,8 @@ def forward_fp8(q, k, v_t, q_descale=1.0, k_descale=1.0, v_descale=1.0, scale=No
     transposed (ldv >= N, a multiple of 16). scale defaults to 1/sqrt(d).
     """
     for t in (q, k, v_t):
-        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError("q, k, v_t must be contiguous uint8 (E4M3 code) GPU tensors of rank 4")
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v_t must be contiguous uint8 (E4M3 code) tensors of rank 4")
     if q.shape != k.shape:
         raise ValueError("q and k must have the same shape")
     B, H, N, d = q.shape
@@ -415,6 +476,11 @@ def forward_fp8(q, k, v_t, q_descale=1.0, k_descale=1.0, v_descale=1.0, scale=No
         raise ValueError("v_t must be [B, H, d, ldv]")
     ldv = v_t.shape[3]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is not None:
+        _need(out, "out", (B, H, N, d), torch.bfloat16)
+    if lse is not None:
+        _need(lse, "lse", (B, H, N), torch.float32)
+    _on_gpu(q.device, q=q, k=k, v_t=v_t, out=out, lse=lse)
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v_t.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, ldv,

@@ -3,13 +3,19 @@ invalid arguments with the documented status before touching the GPU.
 
 CPU only: every call below fails host-side validation, which runs before any
 HIP API call, so no device is needed (pointers are fake, never dereferenced).
+Where a GPU is visible the module is skipped: a regression in the host-side
+validation must fail a test here, never launch a kernel on a fake address.
 """
 import math
 import os
 
 import pytest
+import torch
 
 import io_aware_exact_10_amd as fa
+
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="fake device pointers: host-validation tests run on the CPU build only")
 
 A = 0x10000          # fake, 16-byte aligned "device" addresses
 BIG = 1 << 30        # spacing so fake tensors never overlap
@@ -155,6 +161,63 @@ def test_torch_wrappers_reject_bad_tensors():
         fa.forward(q[0], q[0], q[0])                  # wrong rank
     with pytest.raises(ValueError):
         fa.forward(q, q.float(), q)                   # mixed dtypes
+
+
+def test_torch_wrappers_reject_bad_outputs():
+    """Caller-supplied outputs and workspaces are checked for shape, dtype and
+    contiguity before anything is enqueued: the kernels write through raw
+    pointers, so an undersized buffer would be written past its end."""
+    bf = torch.bfloat16
+    q = torch.zeros(2, 3, 8, 64, dtype=bf)
+    lse = torch.zeros(2, 3, 8)
+    with pytest.raises(ValueError, match="lse"):
+        fa.forward(q, q, q, lse=torch.empty(1))
+    with pytest.raises(ValueError, match="lse"):
+        fa.forward(q, q, q, lse=torch.empty(2, 3, 8, dtype=bf))
+    with pytest.raises(ValueError, match="out"):
+        fa.forward(q, q, q, out=torch.empty(2, 3, 8, 32, dtype=bf))
+    with pytest.raises(ValueError, match="out"):
+        fa.forward(q, q, q, out=torch.empty(2, 3, 8, 64))                       # fp32 out for bf16 q
+    with pytest.raises(ValueError, match="out"):
+        fa.forward(q, q, q, out=torch.empty(2, 3, 64, 8, dtype=bf).transpose(2, 3))  # not contiguous
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward(q, q, q, out=torch.empty_like(q), lse=lse)                   # well formed, on the CPU
+    for name in ("dq", "dk", "dv"):
+        with pytest.raises(ValueError, match=name):
+            fa.backward(q, q, q, q, lse, q, **{name: torch.empty(1, 3, 8, 64, dtype=bf)})
+    with pytest.raises(ValueError, match="lse"):
+        fa.backward(q, q, q, q, torch.zeros(2, 3, 7), q)
+    with pytest.raises(ValueError, match="do"):
+        fa.backward(q, q, q, q, lse, q[:, :, :4].contiguous())
+    with pytest.raises(ValueError, match="workspace"):
+        fa.backward(q, q, q, q, lse, q, workspace=torch.empty(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="GPU"):
+        fa.backward(q, q, q, q, lse, q)
+    # packed batches, split keys, FP8
+    pq = torch.zeros(8, 4, 64, dtype=bf)
+    pk = torch.zeros(8, 2, 64, dtype=bf)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError, match="lse"):
+        fa.forward_varlen(pq, pk, pk, cu, cu, 8, 8, lse=torch.empty(4, 7))
+    with pytest.raises(ValueError, match="out"):
+        fa.forward_varlen(pq, pk, pk, cu, cu, 8, 8, out=torch.empty_like(pk))
+    plse = torch.zeros(4, 8)
+    with pytest.raises(ValueError, match="dk"):
+        fa.backward_varlen(pq, pk, pk, pq, plse, pq, cu, cu, 8, 8, dk=torch.empty_like(pq))
+    with pytest.raises(ValueError, match="workspace"):
+        fa.backward_varlen(pq, pk, pk, pq, plse, pq, cu, cu, 8, 8, workspace=torch.empty(4, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="lse"):
+        fa.forward_splitkv(pq, pk, pk, cu, cu, 8, 8, lse=torch.empty(8, 4))
+    with pytest.raises(ValueError, match="workspace"):
+        fa.forward_splitkv(pq, pk, pk, cu, cu, 8, 8, workspace=torch.empty(4, dtype=torch.uint8))
+    q8 = torch.zeros(1, 2, 16, 64, dtype=torch.uint8)
+    vt8 = torch.zeros(1, 2, 64, 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="out"):
+        fa.forward_fp8(q8, q8, vt8, out=torch.empty(1, 2, 16, 64))
+    with pytest.raises(ValueError, match="lse"):
+        fa.forward_fp8(q8, q8, vt8, lse=torch.empty(1, 2, 15))
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward_fp8(q8, q8, vt8)
 
 
 def test_product_path_does_not_reference_the_oracle():

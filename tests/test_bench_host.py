@@ -101,3 +101,46 @@ def test_hbm_rate():
     assert bench.hbm_rate(None, 1.0) is None
     assert bench.hbm_rate(8e9, 1.0) == 8000.0            # 8 GB in 1 ms
     assert bench.hbm_rate(541e6, 0.3445) == round(541e6 / 0.3445e-3 / 1e9, 1)
+
+
+# --------------------------------------------------------------------------
+# the materialise-S comparator computes attention: its O and gradients
+# against the oracle, for every mask kind ("FlashAttention and IO-aware exact
+# attention", "How to approach it": the naive and the blockwise result on the
+# same random inputs)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("mask_kind", [synth.MASK_NONE, synth.MASK_CAUSAL, synth.MASK_BLOCK_SPARSE])
+@pytest.mark.parametrize("dtype", ["f64", "bf16"])
+def test_naive_comparator_matches_oracle(mask_kind, dtype):
+    import torch
+    w = synth.small_workload(2, 3, 300, 16, synth.DTYPE_BF16, mask_kind, seed=61)
+    inp = synth.make_inputs(w)
+    tdt = torch.float64 if dtype == "f64" else torch.bfloat16
+    # inp.q etc. hold the bf16-rounded values; both dtypes see exactly them
+    q, k, v, do = (torch.from_numpy(np.ascontiguousarray(a)).to(tdt) for a in (inp.q, inp.k, inp.v, inp.do))
+    mask_t = torch.from_numpy(inp.mask) if inp.mask is not None else None
+    bm = bench.naive_mask(w, mask_t, torch.device("cpu"))
+    o, grads = bench.naive_step(q, k, v, do, w.scale, w.mask_kind, bm, True)
+    O, _ = oracle.forward(inp.q, inp.k, inp.v, w.scale, w.mask_kind, inp.mask)
+    ref = (O,) + oracle.backward(inp.q, inp.k, inp.v, inp.do, w.scale, w.mask_kind, inp.mask)
+    got = [t.double().numpy().reshape(r.shape) for t, r in zip((o,) + grads, ref)]
+    # f64: the comparator keeps its softmax in fp32 (P is rounded there);
+    # bf16: the bf16 tolerances the kernels meet (O 2e-2, gradients 5e-2 max-normalised)
+    o_tol, g_tol = (1e-5, 1e-5) if dtype == "f64" else (2e-2, 5e-2)
+    assert np.abs(got[0] - ref[0]).max() <= o_tol
+    for g, r in zip(got[1:], ref[1:]):
+        assert np.abs(g - r).max() / max(np.abs(r).max(), 1e-3) <= g_tol
+    # the comparator materialises the full N x N score matrix of each head
+    assert bm is None or tuple(bm.shape) == (w.N, w.N)
+
+
+@pytest.mark.parametrize("mask_kind", [synth.MASK_NONE, synth.MASK_CAUSAL, synth.MASK_BLOCK_SPARSE])
+def test_visible_pairs_of_a_row_sample_match_oracle_mask(mask_kind):
+    """The CPU baseline credits the oracle with the visible pairs of exactly
+    the rows it samples."""
+    N = 700
+    w = synth.small_workload(1, 1, N, 64, synth.DTYPE_BF16, mask_kind, seed=71)
+    inp = synth.make_inputs(w)
+    rows = np.arange(0, N, 7)
+    vis = oracle.visible(rows, N, mask_kind, inp.mask)
+    assert bench.visible_pairs_rows(w, inp.mask, rows) == int(vis.sum())

@@ -500,3 +500,91 @@ def test_no_keys_at_all():
         assert (dq == 0).all() and dk.shape == (0, 4) and dv.shape == (0, 4)
     O, L = oracle.forward_varlen(rnd(323, 2, 2, 4), np.zeros((0, 1, 4)), np.zeros((0, 1, 4)), [0, 2], [0, 0], 0.5)
     assert (O == 0).all() and np.isneginf(L).all()
+
+
+# --------------------------------------------------------------------------
+# batched wrappers and the sampled-rows path, against torch float64 SDPA run
+# over whole [B, H, N, d] tensors (torch handles the batch and head axes
+# itself, so a (b, h) ordering slip in the oracle's stacking shows up)
+# --------------------------------------------------------------------------
+def _vis_independent(nq, nk, mask_kind, bm, blk, offset=0):
+    """Visibility written out from the mask definitions, not via the oracle."""
+    i, j = np.meshgrid(np.arange(nq), np.arange(nk), indexing="ij")
+    if mask_kind == MASK_CAUSAL:
+        return j <= i + offset
+    if mask_kind == MASK_BLOCK_SPARSE:
+        return bm[i // blk, j // blk] != 0
+    return np.ones((nq, nk), dtype=bool)
+
+
+def _torch_ref_batched(q, k, v, do, scale, vis):
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    m = torch.tensor(vis)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=scale)
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    s = (scale * (tq @ tk.transpose(-1, -2))).masked_fill(~m, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return (out.detach().numpy(), lse.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy())
+
+
+@pytest.mark.parametrize("mask_kind", [MASK_NONE, MASK_CAUSAL, MASK_BLOCK_SPARSE])
+def test_batched_wrappers_match_sdpa_over_batch_and_heads(mask_kind):
+    """oracle.forward / oracle.backward stack their heads in (b, h) order,
+    h fastest, and a ``heads`` list selects and orders them. B != H (both
+    > 1) and every head holds different numbers, so a swapped or shifted
+    head index fails."""
+    B, H, N, d, blk = 2, 3, 19, 4, 4
+    rng = np.random.default_rng(41)
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    bm = rand_block_mask(42, -(-N // blk)) if mask_kind == MASK_BLOCK_SPARSE else None
+    scale = 0.6
+    vis = _vis_independent(N, N, mask_kind, bm, blk)
+    ro, rl, rdq, rdk, rdv = _torch_ref_batched(q, k, v, do, scale, vis)
+    O, L = oracle.forward(q, k, v, scale, mask_kind, bm, block=blk)
+    dq, dk, dv = oracle.backward(q, k, v, do, scale, mask_kind, bm, block=blk)
+    assert O.shape == (B * H, N, d) and L.shape == (B * H, N)
+    for a, b in ((O, ro), (L, rl), (dq, rdq), (dk, rdk), (dv, rdv)):
+        assert np.abs(a - b.reshape(a.shape)).max() <= 1e-12 * max(1.0, np.abs(b).max())
+    heads = [(1, 2), (0, 0), (1, 0), (0, 2)]
+    O2, L2 = oracle.forward(q, k, v, scale, mask_kind, bm, heads=heads, block=blk)
+    g2 = oracle.backward(q, k, v, do, scale, mask_kind, bm, heads=heads, block=blk)
+    for i, (b, h) in enumerate(heads):
+        assert np.abs(O2[i] - ro[b, h]).max() <= 1e-12
+        assert np.abs(L2[i] - rl[b, h]).max() <= 1e-12
+        for g, ref in zip(g2, (rdq, rdk, rdv)):
+            assert np.abs(g[i] - ref[b, h]).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+    # a row sample through the batched wrapper: same rows of every selected head
+    rows = np.array([17, 3, 11, 0, 18])
+    O3, L3 = oracle.forward(q, k, v, scale, mask_kind, bm, heads=heads, rows=rows, block=blk)
+    for i, (b, h) in enumerate(heads):
+        assert np.abs(O3[i] - ro[b, h][rows]).max() <= 1e-12
+        assert np.abs(L3[i] - rl[b, h][rows]).max() <= 1e-12
+
+
+@pytest.mark.parametrize("case", ["none", "causal", "block_sparse", "causal_offset"])
+def test_forward_head_row_sample_equals_full_rows(case):
+    """forward_head(rows=...) on a shuffled, duplicate-free row sample that
+    crosses several ``chunk`` boundaries gives exactly the sampled rows of
+    the full result, in sample order. Visibility must follow each row's
+    position in the sequence (not in the sample) and each chunk's LSE must
+    land in its own slots; SDPA on the full problem pins both."""
+    mask_kind = {"none": MASK_NONE, "causal": MASK_CAUSAL, "block_sparse": MASK_BLOCK_SPARSE,
+                 "causal_offset": MASK_CAUSAL}[case]
+    nq, nk, d, blk = (37, 53, 6, 8) if case == "causal_offset" else (45, 45, 6, 8)
+    rng = np.random.default_rng(43)
+    q, do = rng.standard_normal((nq, d)), rng.standard_normal((nq, d))
+    k, v = rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    bm = rand_block_mask(44, -(-nk // blk)) if mask_kind == MASK_BLOCK_SPARSE else None
+    scale = 0.9
+    offset = nk - nq
+    vis = _vis_independent(nq, nk, mask_kind, bm, blk, offset)
+    ro, rl, _, _, _ = _torch_ref_batched(q, k, v, do, scale, vis)
+    rows = rng.permutation(nq)[:29]
+    assert len(set(rows.tolist())) == rows.size and not (np.diff(rows) > 0).all()
+    Of, Lf = oracle.forward_head(q, k, v, scale, mask_kind, bm, block=blk)
+    for chunk in (1, 6, 7, 29, 2048):
+        Os, Ls = oracle.forward_head(q, k, v, scale, mask_kind, bm, rows=rows, block=blk, chunk=chunk)
+        assert Os.shape == (rows.size, d) and Ls.shape == (rows.size,)
+        assert np.abs(Os - ro[rows]).max() <= 1e-12, chunk
+        assert np.abs(Ls - rl[rows]).max() <= 1e-12, chunk
+        assert np.abs(Os - Of[rows]).max() <= 1e-13 and np.abs(Ls - Lf[rows]).max() <= 1e-13
