@@ -181,9 +181,18 @@ __device__ __forceinline__ u32x4 row_frag(const uint8_t* tile_row0, int base, in
 // of the 8-byte chunks addressed by lanes 4 j + i / 4 (j = 0..3), so lane s
 // of group g addresses row 8 sel + 4 (g / 2) + (s % 16) / 4, columns
 // 16 (g % 2) + 4 (s % 4) (col_frag_base).
+//
+// The transpose read goes through tr_read, whose pointer is __restrict__: once
+// inlined, the read carries alias-scope metadata like an ordinary load, so the
+// compiler no longer waits for every global->LDS copy in flight (vmcnt(0))
+// before it. The copies target the other LDS buffer; the explicit
+// wait_vmem() + barrier at the end of each tile orders them with the reads.
+__device__ __forceinline__ i16x4 tr_read(lds_i16x4* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+}
 __device__ __forceinline__ u32x4 col_frag(const uint8_t* tile_row0, int base0, int base1, int dt) {
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_row0 + (base0 ^ (64 * dt))));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_row0 + (base1 ^ (64 * dt))));
+  const i16x4 a = tr_read((lds_i16x4*)(tile_row0 + (base0 ^ (64 * dt))));
+  const i16x4 b = tr_read((lds_i16x4*)(tile_row0 + (base1 ^ (64 * dt))));
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
