@@ -48,8 +48,9 @@
  *   `stream` (asynchronous); FA_ERR_HIP means a launch failed (the HIP error
  *   is not cleared). A device fault surfaces at the caller's next
  *   synchronisation.
- * State. No global mutable state; calls are thread-safe. Results are
- *   bitwise deterministic from run to run (no atomics).
+ * State. No global mutable state (fa_bwd_noalloc aside: it uses one
+ *   library-owned scratch array per GPU); calls are thread-safe. Results
+ *   are bitwise deterministic from run to run (no atomics).
  */
 #ifndef FA_H_
 #define FA_H_
@@ -71,7 +72,8 @@ typedef enum {
   FA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_ALIGN = -6,       /* a pointer is not aligned as stated above */
   FA_ERR_HIP = -7,         /* a kernel launch returned a HIP error */
-  FA_ERR_ARG = -8          /* non-finite scale, or an output overlaps another tensor */
+  FA_ERR_ARG = -8,         /* non-finite scale, or an output overlaps another tensor */
+  FA_ERR_SCRATCH = -9      /* fa_bwd_noalloc: B * H * N exceeds FA_BWD_NOALLOC_MAX_ROWS */
 } fa_status;
 
 typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_BLOCK_SPARSE = 2 } fa_mask_kind;
@@ -285,6 +287,32 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* ls
 
 /* Static, human-readable name of a fa_status value ("unknown status" otherwise). */
 const char* fa_status_string(int status);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code recorded into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc. It computes exactly what fa_bwd computes
+ * (the same three kernels, bitwise the same dq, dk, dv) and allocates
+ * nothing: the row term and the rescaled LSE that fa_bwd keeps in the
+ * caller's workspace go to a scratch array inside the library's device code,
+ * one copy per GPU, allocated when the library's code is loaded on that GPU
+ * and held until the process ends. Its address on the current device is
+ * looked up once per device, on that device's first call.
+ *   Limit. B * H * N <= FA_BWD_NOALLOC_MAX_ROWS (2^21 query rows, 16 MiB of
+ *   scratch); larger problems return FA_ERR_SCRATCH (checked before any
+ *   other argument) and nothing is enqueued (use fa_bwd with a workspace).
+ *   Sharing. Every call on one GPU uses that GPU's single scratch array, and
+ *   each call overwrites every entry it reads before reading it. Calls that
+ *   can overlap in time on one GPU (other streams, other threads) race on
+ *   the array and must be serialised by the caller.
+ * Arguments, layout, validation and the other errors are those of fa_bwd;
+ * FA_ERR_HIP also covers a failed lookup of the scratch address.
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS (1 << 21)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale,
+                   int mask_kind, const uint8_t* block_mask, int dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -26,12 +26,12 @@ import torch  # loads the HIP runtime first, so libfa.so binds to the same one
 
 __all__ = [
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_MASK",
-    "FA_ERR_WORKSPACE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_ARG",
+    "FA_ERR_WORKSPACE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_ARG", "FA_ERR_SCRATCH", "FA_BWD_NOALLOC_MAX_ROWS",
     "MASK_NONE", "MASK_CAUSAL", "MASK_BLOCK_SPARSE", "DTYPE_BF16", "DTYPE_F32",
     "FAError", "fa_fwd", "fa_fwd_tiled", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen", "fa_bwd_varlen",
     "fa_bwd_varlen_workspace_bytes", "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
-    "fa_fwd_fp8", "forward", "backward", "forward_varlen", "backward_varlen", "forward_splitkv", "forward_fp8",
+    "fa_fwd_fp8", "fa_bwd_noalloc", "forward", "backward", "backward_noalloc", "forward_varlen", "backward_varlen", "forward_splitkv", "forward_fp8",
     "library_path", "lib",
 ]
 
@@ -40,7 +40,8 @@ LIB_PATH = os.path.join(_PKG, "libfa.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "fa.h")
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
-FA_ERR_MASK, FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_ARG = -4, -5, -6, -7, -8
+FA_ERR_MASK, FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_ARG, FA_ERR_SCRATCH = -4, -5, -6, -7, -8, -9
+FA_BWD_NOALLOC_MAX_ROWS = 1 << 21   # B * H * N limit of fa_bwd_noalloc (its built-in scratch)
 MASK_NONE, MASK_CAUSAL, MASK_BLOCK_SPARSE = 0, 1, 2
 DTYPE_BF16, DTYPE_F32 = 0, 1
 MASK_BLOCK = 128
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_splitkv.restype = i
         L.fa_fwd_fp8.argtypes = [vp] * 5 + [i] * 5 + [f, f, f, f, i, vp]
         L.fa_fwd_fp8.restype = i
+        L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
+        L.fa_bwd_noalloc.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -136,6 +139,12 @@ def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, mask_kind, block_
            workspace, workspace_bytes, stream) -> int:
     return int(lib().fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, ctypes.c_float(scale),
                             mask_kind, block_mask, dtype, workspace, workspace_bytes, stream))
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, mask_kind, block_mask, dtype,
+                   stream) -> int:
+    return int(lib().fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, ctypes.c_float(scale),
+                                    mask_kind, block_mask, dtype, stream))
 
 
 def fa_bwd_rowterm(o, dO, lse, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
@@ -344,6 +353,33 @@ def backward(q, k, v, o, lse, do, scale=None, mask_kind=MASK_NONE, block_mask=No
         raise ValueError(f"unknown steps {steps!r}")
     if st != FA_OK:
         raise FAError(st, f"fa_bwd ({steps})")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, lse, do, scale=None, mask_kind=MASK_NONE, block_mask=None, dq=None, dk=None,
+                     dv=None):
+    """``backward`` through fa_bwd_noalloc: no workspace (the library's
+    built-in per-GPU scratch holds the row statistics), so with dq, dk, dv
+    passed in nothing is allocated. B * H * N <= FA_BWD_NOALLOC_MAX_ROWS."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    _need(o, "o", q.shape, q.dtype)
+    _need(do, "do", q.shape, q.dtype)
+    _need(lse, "lse", (B, H, N), torch.float32)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None:
+            _need(t, name, q.shape, q.dtype)
+    _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    mp = _mask_ptr(mask_kind, block_mask, N, q.device)
+    st = fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, mask_kind, mp,
+                        _DT[q.dtype], _stream(q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fa.h"
 #include "fa_kernels.h"
 
@@ -90,6 +92,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIGN: return "misaligned pointer (tensors 16-byte, lse 4-byte aligned)";
     case FA_ERR_HIP: return "HIP kernel launch failed";
     case FA_ERR_ARG: return "invalid argument (non-finite scale or overlapping output)";
+    case FA_ERR_SCRATCH:
+      return "fa_bwd_noalloc: B * H * N exceeds FA_BWD_NOALLOC_MAX_ROWS (use fa_bwd with a workspace)";
     default: return "unknown status";
   }
 }
@@ -152,7 +156,14 @@ const void* const unused = &kUnusedTag;
 int bwd_prepare(const void* q, const void* k, const void* v, const void* o, const float* lse,
                 const void* dO, const void* dq, const void* dk, const void* dv,
                 int B, int H, int N, int d, float scale, int mask_kind, const uint8_t* block_mask,
-                int dtype, const void* workspace, size_t workspace_bytes, fa::AttnParams* out) {
+                int dtype, const void* workspace, size_t workspace_bytes, fa::AttnParams* out,
+                bool builtin_scratch = false) {
+  // builtin_scratch: the workspace is the library's own scratch array (no
+  // caller pointer to check); the caller of this function sets dterm / lse2.
+  if (builtin_scratch) {
+    workspace = unused;
+    workspace_bytes = 0;
+  }
   const void* tens[8] = {q, k, v, o, dO, dq, dk, dv};
   for (const void* t : tens)
     if (!t) return FA_ERR_NULL;
@@ -161,11 +172,11 @@ int bwd_prepare(const void* q, const void* k, const void* v, const void* o, cons
   int st = check_common(B, H, N, d, scale, mask_kind, block_mask, dtype, &elems);
   if (st != FA_OK) return st;
   const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!builtin_scratch && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
   for (const void* t : tens)
     if (t != unused && !aligned(t, 16)) return FA_ERR_ALIGN;
   if ((const void*)lse != unused && !aligned(lse, 4)) return FA_ERR_ALIGN;
-  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+  if (!builtin_scratch && !aligned(workspace, 16)) return FA_ERR_ALIGN;
   const size_t tb = (size_t)elems * (dtype == FA_BF16 ? 2 : 4);
   const size_t lb = (size_t)B * H * N * sizeof(float);
   const void* ins[6] = {q, k, v, o, dO, lse};
@@ -190,8 +201,10 @@ int bwd_prepare(const void* q, const void* k, const void* v, const void* o, cons
   p.dq = const_cast<void*>(take(dq));
   p.dk = const_cast<void*>(take(dk));
   p.dv = const_cast<void*>(take(dv));
-  p.dterm = (float*)const_cast<void*>(workspace);
-  p.lse2 = (float*)((uint8_t*)const_cast<void*>(workspace) + row_array_bytes((size_t)B * H * N));
+  if (!builtin_scratch) {
+    p.dterm = (float*)const_cast<void*>(workspace);
+    p.lse2 = (float*)((uint8_t*)const_cast<void*>(workspace) + row_array_bytes((size_t)B * H * N));
+  }
   *out = p;
   return FA_OK;
 }
@@ -243,6 +256,71 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, con
   const int st = bwd_prepare(q, k, v, unused, lse, dO, dq, unused, unused, B, H, N, d, scale, mask_kind, block_mask,
                              dtype, workspace, workspace_bytes, &p);
   return st != FA_OK ? st : bwd_launch(p, mask_kind, dtype, fa::kBwdDq, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// allocation-free backward: the workspace lives in a library-owned array
+// ---------------------------------------------------------------------------
+// The row term and the rescaled LSE of up to FA_BWD_NOALLOC_MAX_ROWS query
+// rows (two float arrays, each a multiple of 256 bytes). The code object
+// holds one copy per GPU it is loaded on, for the life of the process. In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// only the per-device address from hipGetSymbolAddress is passed on.
+namespace {
+constexpr size_t kScratchRows = (size_t)FA_BWD_NOALLOC_MAX_ROWS;
+constexpr size_t kScratchBytes = 2 * kScratchRows * sizeof(float);
+static_assert(kScratchRows * sizeof(float) % 256 == 0, "each array a multiple of 256 bytes");
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];   // device address of `scratch`, per device ordinal
+
+// Address of this GPU's scratch array, looked up on the device's first call
+// with that device current. Concurrent first calls look it up twice and store
+// the same value.
+int scratch_on_current_device(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  void* a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) return FA_ERR_HIP;
+    g_scratch_addr[dev].store(a, std::memory_order_release);
+  }
+  *out = (uint8_t*)a;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale,
+                   int mask_kind, const uint8_t* block_mask, int dtype, hipStream_t stream) {
+  // The row limit first: a problem past it is rejected whatever else is wrong.
+  const size_t rows = (size_t)(B > 0 ? B : 0) * (size_t)(H > 0 ? H : 0) * (size_t)(N > 0 ? N : 0);
+  if (rows > kScratchRows) return FA_ERR_SCRATCH;
+  fa::AttnParams p;
+  int st = bwd_prepare(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, mask_kind, block_mask, dtype,
+                       nullptr, 0, &p, /*builtin_scratch=*/true);
+  if (st != FA_OK) return st;
+  uint8_t* base = nullptr;
+  st = scratch_on_current_device(&base);
+  if (st != FA_OK) return st;
+  // Same split as fa_bwd's workspace: the row term, then the rescaled LSE.
+  // The row-term kernel writes both for every row before the other two
+  // kernels (later on the same stream) read them, so the previous call's
+  // contents never reach a result and nothing needs clearing.
+  p.dterm = (float*)base;
+  p.lse2 = (float*)(base + row_array_bytes(rows));
+  return bwd_launch(p, mask_kind, dtype, fa::kBwdAll, stream);
 }
 
 }  // extern "C"

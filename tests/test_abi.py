@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"fa_fwd", "fa_fwd_tiled", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen",
                           "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_splitkv_splits",
-                          "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_fp8"}
+                          "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_bwd_noalloc"}
     L = fa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -71,7 +71,7 @@ def test_single_hip_runtime_in_process():
 
 def test_status_strings():
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_MASK,
-             fa.FA_ERR_WORKSPACE, fa.FA_ERR_ALIGN, fa.FA_ERR_HIP, fa.FA_ERR_ARG]
+             fa.FA_ERR_WORKSPACE, fa.FA_ERR_ALIGN, fa.FA_ERR_HIP, fa.FA_ERR_ARG, fa.FA_ERR_SCRATCH]
     seen = set()
     for c in codes:
         s = fa.fa_status_string(c)
@@ -161,6 +161,32 @@ def test_torch_wrappers_reject_bad_tensors():
         fa.forward(q[0], q[0], q[0])                  # wrong rank
     with pytest.raises(ValueError):
         fa.forward(q, q.float(), q)                   # mixed dtypes
+
+
+def noalloc_args(**kw):
+    a = bwd_args()
+    del a["workspace"], a["workspace_bytes"]
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(dv=None), fa.FA_ERR_NULL),
+    (dict(N=0), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask_kind=2, block_mask=None), fa.FA_ERR_MASK),
+    (dict(scale=math.inf), fa.FA_ERR_ARG),
+    (dict(dq=A + 8), fa.FA_ERR_ALIGN),
+    (dict(dk=A + 2 * BIG), fa.FA_ERR_ARG),                         # dk aliases v
+    # one row past the built-in scratch; the tensors (256 MiB each) still fit the fake 1 GiB spacing
+    (dict(B=1, H=1, N=fa.FA_BWD_NOALLOC_MAX_ROWS + 1), fa.FA_ERR_SCRATCH),
+    (dict(B=2, H=16, N=fa.FA_BWD_NOALLOC_MAX_ROWS // 32 + 64, d=64), fa.FA_ERR_SCRATCH),
+])
+def test_bwd_noalloc_validation(kw, code):
+    """fa_bwd_noalloc validates like fa_bwd (no workspace arguments) and
+    rejects problems past its built-in scratch before any HIP call."""
+    assert fa.fa_bwd_noalloc(**noalloc_args(**kw)) == code
 
 
 def test_torch_wrappers_reject_bad_outputs():
