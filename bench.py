@@ -580,7 +580,7 @@ def main() -> int:
             torch.cuda.synchronize()
             nms = e0.elapsed_time(e1) / reps
             naive = {"ms_per_step": round(nms, 3), "tflops": round((fwd_flop + bwd_flop) / (nms * 1e-3) / 1e12, 2),
-                     "what": "torch matmul, mask, softmax (fp32), matmul; autograd backward"
+                     "what": "torch matmul, mask, softmax (fp32), matmul" + ("; autograd backward" if backward else "")
                              + ("; one head at a time" if w.N > NAIVE_WHOLE_N else "")}
         except Exception as ex:  # noqa: BLE001
             naive = {"error": repr(ex)[:200]}

@@ -1,7 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times: the whole batch runs on the GPU through the C ABI, and the
-oracle recomputes sampled heads (all rows, or sampled rows for the 32K
-prefill) one by one for comparison.
+oracle recomputes sampled heads (all rows), or for the 32K prefill every
+head on sampled rows, one by one for comparison.
 """
 import numpy as np
 import pytest
@@ -32,11 +32,13 @@ def test_workload_sampled_heads(name):
     torch.cuda.synchronize()
     assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
     rows = None
+    heads = sampled_heads(w)
     if w.N > 8192:
-        rng = np.random.default_rng(w.seed)
-        rows = np.unique(np.concatenate([np.arange(256), np.arange(w.N - 256, w.N),
-                                         rng.choice(w.N, 256, replace=False)]))
-    for b, h in sampled_heads(w):
+        # long sequences: every head, on every 64th query row plus the first
+        # and the last 64 rows (the shortest and the longest causal rows)
+        rows = np.unique(np.concatenate([np.arange(0, w.N, 64), np.arange(64), np.arange(w.N - 64, w.N)]))
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in heads:
         O, L = oracle.forward_head(inp.q[b, h], inp.k[b, h], inp.v[b, h], w.scale, w.mask_kind, inp.mask, rows)
         go = o[b, h].float().cpu().numpy()
         gl = lse[b, h].cpu().numpy()
