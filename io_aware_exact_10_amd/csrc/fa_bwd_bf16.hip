@@ -153,9 +153,9 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     ld.load(sm.dO[buf], dOg + j * p.q_hs, q0, Nq);
     if (w < 2) {   // one dword per lane: 64 row statistics per tile
       const int q = min(q0 + lane, Nq - 1);
-      const float* src = (w == 0 ? lseg : dtg) + j * p.l_hs + q;
+      const float* src = (w == 0 ? lseg : dtg) + j * p.l_hs;
       float* dst = w == 0 ? sm.lse[buf] : sm.dterm[buf];
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 4, 0, 0);
+      copy_to_lds<false>(src, q * 4, dst);
     }
   };
 
@@ -173,6 +173,11 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
     kf[ks] = a ^ p.qflip;   // S = |scale| Q (sign(scale) K)^T: the sign of scale rides on K here
     vf[ks] = b;
   }
+  // Complete these loads here: the compiler would otherwise wait for them at
+  // their first use inside the tile loop, in every iteration, and that wait
+  // (vmcnt) would also wait for the next tile's copies in flight.
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(kf[ks]), "+v"(vf[ks]));
 
   f32x16 dkT[NDT], dvT[NDT];
 #pragma unroll
@@ -436,6 +441,10 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     nl = p.lse2[li];
     ndt = p.dterm[li];
   }
+  // Complete these loads before the tile loop (see the dK/dV kernel).
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qf[ks]), "+v"(of[ks]));
+  asm volatile("" : "+v"(nl), "+v"(ndt));
 
   f32x16 dqT[NDT];
 #pragma unroll

@@ -71,6 +71,32 @@ __device__ __forceinline__ int tile_off(int r, int col) {
   return r * (D * 2) + ((((col >> 3) ^ swz<D>(r))) << 4) + ((col & 7) << 1);
 }
 
+// One global->LDS copy instruction (16 bytes per lane, or 4 with DW4 =
+// false): lane i's bytes go to LDS byte address lds + 16 i (4 i). Written out
+// so the compiler does not track the copy: it would otherwise wait for it
+// (or coarsen every LDS wait) before each later LDS read, though every
+// kernel orders its copies and reads itself (wait_vmem() and a barrier
+// before any wave reads a buffer a copy writes). The instruction has no
+// register result; M0 holds the LDS address, and one wait state separates
+// the M0 write from the copy.
+template <bool DW4 = true>
+__device__ __forceinline__ void copy_to_lds(const void* gbase, int voff, const void* lds) {
+  // Both bases are the same in every lane (the callers pass workgroup- or
+  // wave-uniform values); readfirstlane states it where the compiler cannot
+  // prove it, so they go to scalar registers as the instruction requires.
+  const uint64_t gb = (uint64_t)(uintptr_t)gbase;
+  const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)gb);
+  const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(gb >> 32));
+  gbase = (const void*)(((uint64_t)ghi << 32) | glo);
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  if (DW4)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(m)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(gbase), "s"(m)
+                 : "memory", "m0");
+}
+
 // Asynchronous copy of rows [r0, r0 + ROWS) of an N-row bf16 matrix with D
 // columns and a row stride of rsb bytes into a swizzled LDS tile, straight
 // from global memory to LDS (no registers). Each wave instruction fills one
@@ -117,16 +143,13 @@ struct TileLoader {
     const uint8_t* base = (const uint8_t*)X + (int64_t)r0 * rsb;
     if (r0 + ROWS <= N) {
 #pragma unroll
-      for (int i = 0; i < PER; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(base + offs[i]), (lds_void*)(tile + (wave + i * NWAVES) * 1024),
-                                         16, 0, 0);
+      for (int i = 0; i < PER; ++i) copy_to_lds(base, offs[i], tile + (wave + i * NWAVES) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         int o = offs[i];
         if (r0 + row_of(wave, lane_, i) >= N) o = (N - 1 - r0) * rsb + (chunk_of(wave, lane_, i) << 4);
-        __builtin_amdgcn_global_load_lds((const void*)(base + o), (lds_void*)(tile + (wave + i * NWAVES) * 1024),
-                                         16, 0, 0);
+        copy_to_lds(base, o, tile + (wave + i * NWAVES) * 1024);
       }
     }
   }
@@ -181,18 +204,9 @@ __device__ __forceinline__ u32x4 row_frag(const uint8_t* tile_row0, int base, in
 // of the 8-byte chunks addressed by lanes 4 j + i / 4 (j = 0..3), so lane s
 // of group g addresses row 8 sel + 4 (g / 2) + (s % 16) / 4, columns
 // 16 (g % 2) + 4 (s % 4) (col_frag_base).
-//
-// The transpose read goes through tr_read, whose pointer is __restrict__: once
-// inlined, the read carries alias-scope metadata like an ordinary load, so the
-// compiler no longer waits for every global->LDS copy in flight (vmcnt(0))
-// before it. The copies target the other LDS buffer; the explicit
-// wait_vmem() + barrier at the end of each tile orders them with the reads.
-__device__ __forceinline__ i16x4 tr_read(lds_i16x4* __restrict__ p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
-}
 __device__ __forceinline__ u32x4 col_frag(const uint8_t* tile_row0, int base0, int base1, int dt) {
-  const i16x4 a = tr_read((lds_i16x4*)(tile_row0 + (base0 ^ (64 * dt))));
-  const i16x4 b = tr_read((lds_i16x4*)(tile_row0 + (base1 ^ (64 * dt))));
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_row0 + (base0 ^ (64 * dt))));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_row0 + (base1 ^ (64 * dt))));
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }

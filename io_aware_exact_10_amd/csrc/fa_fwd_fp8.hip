@@ -120,13 +120,11 @@ void fwd_fp8_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
       const int kr = (P * 1024 + 16 * ln) / D;
       const int kc = (ln % (D / 16)) ^ f8_swz_k<D>(kr);
       const int key = min(k0 + f8_key_of_row(kr), N - 1);   // rows past N: a real row, masked
-      __builtin_amdgcn_global_load_lds((const void*)(Kh + (int64_t)key * D + 16 * kc),
-                                       (lds_void*)(sm.k[buf] + P * 1024), 16, 0, 0);
+      copy_to_lds(Kh, key * D + 16 * kc, sm.k[buf] + P * 1024);
       const int vr = 16 * P + (ln >> 2);
       const int vc = (ln & 3) ^ f8_swz_v(vr);
       const int col = min(k0 + 16 * vc, ldv - 16);            // chunks past ldv: keys >= N, zeroed
-      __builtin_amdgcn_global_load_lds((const void*)(Vt + (int64_t)vr * ldv + col),
-                                       (lds_void*)(sm.v[buf] + P * 1024), 16, 0, 0);
+      copy_to_lds(Vt, vr * ldv + col, sm.v[buf] + P * 1024);
     }
   };
 
