@@ -23,7 +23,9 @@
 //                 both as a row operand (S = Q K^T, dP = dO V^T) and, through
 //                 LDS transpose reads, as a column operand (dV^T = dO^T P,
 //                 dK^T = Q^T dS); dK^T and dV^T accumulate in registers and
-//                 are written once.
+//                 are written once. At d = 128 an eight-wave variant runs
+//                 two waves per SIMD: wave pairs split each query tile, V is
+//                 read from LDS, and the pairs' partial sums are added once.
 //   bwd_dq        one workgroup per 128-query tile (32 queries per wave),
 //                 looping over the visible 64-key tiles: Q and dO stay in
 //                 registers; K and V tiles stream through LDS the same way
@@ -45,6 +47,14 @@ namespace fa {
 
 constexpr int kThreads = 256;
 constexpr int kMaskBlk = 128;
+
+// d = 128 dK/dV: the eight-wave kernel (two waves per SIMD, K and V in LDS)
+// when 1, the four-wave kernel (K and V in registers, one wave per SIMD)
+// when 0.
+#ifndef FA_DKDV8
+#define FA_DKDV8 1
+#endif
+
 
 // ---------------------------------------------------------------------------
 // row term D = rowsum(dO * O), fp32 accumulation
@@ -351,6 +361,253 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV at d = 128 with two waves per SIMD: one workgroup of eight waves per
+// 128-key tile. Waves w and w + 4 own the same 32 keys and take the two
+// 32-query halves of every 64-query tile. Each wave keeps its keys' K
+// fragment in registers (the B operand of S = Q K^T); the workgroup's V rows
+// are copied to LDS once and read as the B operand of dP = dO V^T. A wave
+// then holds its dK^T, dV^T accumulators, the K fragment and one half-tile
+// of scores, and two waves fit on each SIMD (the four-wave kernel above keeps
+// K and V in registers, has both halves' scores live and runs one). The two
+// partial accumulators of a key group are summed through LDS at the end, so
+// the keys' gradients are written once.
+// ---------------------------------------------------------------------------
+constexpr int kDkv8Q = 64;       // queries per LDS tile (two halves of 32)
+constexpr int kDkv8Threads = 512;
+
+struct alignas(16) Dkv8Smem {
+  uint8_t v[kDkvBK * 128 * 2];       // the workgroup's V rows, swizzled row-major
+  uint8_t q[2][kDkv8Q * 128 * 2];    // Q tiles
+  uint8_t dO[2][kDkv8Q * 128 * 2];   // dO tiles
+  float lse[2][kDkv8Q];              // -LSE log2(e) of the tile's queries
+  float dterm[2][kDkv8Q];            // -D of the tile's queries
+};
+static_assert(sizeof(Dkv8Smem) <= 160 * 1024, "LDS per workgroup");
+// the final exchange of partial accumulators (dK, then dV) reuses the first
+// 64 KiB
+static_assert(4 * 4 * 16 * 64 * sizeof(float) <= 2 * kDkvBK * 128 * 2, "exchange area");
+
+template <int MASK>
+__global__ __launch_bounds__(kDkv8Threads) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkdv8_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
+  constexpr int D = 128;
+  constexpr int NDT = D / 32;
+  constexpr int QPB = kMaskBlk / kDkv8Q;               // query tiles per mask block
+  __shared__ Dkv8Smem sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r = lane & 31;
+  const int kg = w & 3, half = w >> 2;                  // key group, query half
+  const uint32_t L = xcd_remap(blockIdx.x, total);
+  const uint32_t bh = L / nkt;                          // (K/V head, batch), head-major
+  const int kt = (int)(L - bh * nkt);
+  const int k0 = kt * kDkvBK;
+  const int hk = (int)bh / p.B, bat = (int)bh - hk * p.B;
+  const SeqView sq = seq_view(p, bat);
+  if (k0 >= sq.nk) return;
+  const int Nq = sq.nq, Nk = sq.nk;
+  const int off = Nk - Nq;
+  const int G = p.H / p.Hkv;
+  const int kw0 = k0 + 32 * kg;
+  const int kj = kw0 + r;
+  const uint16_t* __restrict__ Kh = (const uint16_t*)p.k + sq.kb + hk * p.k_hs;
+  const uint16_t* __restrict__ Vh = (const uint16_t*)p.v + sq.kb + hk * p.k_hs;
+  const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + sq.qb + (int64_t)hk * G * p.q_hs;
+  const uint16_t* __restrict__ dOg = (const uint16_t*)p.dO + sq.qb + (int64_t)hk * G * p.q_hs;
+  const float* __restrict__ lseg = p.lse2 + sq.lb + (int64_t)hk * G * p.l_hs;
+  const float* __restrict__ dtg = p.dterm + sq.lb + (int64_t)hk * G * p.l_hs;
+
+  const int nqt = (Nq + kDkv8Q - 1) / kDkv8Q;
+  int qbeg = 0;
+  if (MASK == 1) {
+    const int first = k0 - off;                         // first query that sees key k0
+    qbeg = first <= 0 ? 0 : min(nqt, first / kDkv8Q);
+  }
+  MaskScan ms;
+  if (MASK == 2) ms.init(p.block_mask + kt, p.nblk, p.nblk);
+  auto next_in_head = [&](int it) -> int {
+    if (MASK != 2 || it >= nqt) return it < nqt ? it : nqt;
+    const int blk = it / QPB;
+    const int nb = ms.next(blk);
+    if (nb >= p.nblk) return nqt;
+    const int t = nb == blk ? it : nb * QPB;
+    return t < nqt ? t : nqt;
+  };
+  TileLoader<D, kDkv8Q, 8> ld;
+  ld.init(w, lane, (int)(p.q_rs * 2));
+  auto issue = [&](int it, int j, int buf) {
+    const int q0 = it * kDkv8Q;
+    ld.load(sm.q[buf], Qg + j * p.q_hs, q0, Nq);
+    ld.load(sm.dO[buf], dOg + j * p.q_hs, q0, Nq);
+    if (w < 2) {   // one dword per lane: the tile's 64 row statistics
+      const int q = min(q0 + lane, Nq - 1);
+      copy_to_lds<false>((w == 0 ? lseg : dtg) + j * p.l_hs, q * 4, w == 0 ? sm.lse[buf] : sm.dterm[buf]);
+    }
+  };
+  {
+    // the workgroup's V rows; rows past Nk repeat row Nk - 1, and their
+    // gradients are never written
+    TileLoader<D, kDkvBK, 8> vl;
+    vl.init(w, lane, (int)(p.k_rs * 2));
+    vl.load(sm.v, Vh, k0, Nk);
+  }
+  u32x4 kf[D / 16];   // this lane's key: the B operand of S = Q K^T
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u};
+    if (kj < Nk) a = *(const u32x4*)(Kh + kj * p.k_rs + ks * 16 + h * 8);
+    kf[ks] = a;
+  }
+  // Complete these loads here: the compiler would otherwise wait for them at
+  // their first use inside the tile loop, in every iteration, and that wait
+  // (vmcnt) would also wait for the next tile's copies in flight.
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(kf[ks]));
+  int it = next_in_head(qbeg), j = 0;
+  if (it < nqt) issue(it, j, 0);
+
+  f32x16 dkT[NDT], dvT[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) {
+    dkT[i] = zero16();
+    dvT[i] = zero16();
+  }
+  // P = 2^(c s - LSE log2 e) with s = q . k and c = scale log2(e) (signed:
+  // no max is taken here, so a negative scale needs no operand flip).
+  const float c = p.scale * kLog2e;
+  const int rbase_l = row_frag_base<D>(lane);
+  const int cbase0_l = col_frag_base<D>(lane, 0), cbase1_l = col_frag_base<D>(lane, 1);
+  const uint8_t* sbase = (const uint8_t*)&sm;
+  const int hrow = half * 32 * 2 * D, krow = kg * 32 * 2 * D;   // this half's query rows, this group's key rows
+
+  auto tile = [&](int buf, int q0, auto nm) {
+    constexpr bool NM = decltype(nm)::value;
+    const int qh0 = q0 + 32 * half;                      // this wave's first query
+    if (NM && (qh0 >= Nq || (MASK == 1 && qh0 + 31 + off < kw0))) return;   // nothing visible
+    const int oq = (int)(sm.q[buf] - sbase), oo = (int)(sm.dO[buf] - sbase), ov = (int)(sm.v - sbase);
+    int qr = rbase_l + oq + hrow, orow = rbase_l + oo + hrow, vr = rbase_l + ov + krow;
+    int qc0 = cbase0_l + oq, qc1 = cbase1_l + oq, oc0 = cbase0_l + oo, oc1 = cbase1_l + oo;
+    asm volatile("" : "+v"(qr), "+v"(orow), "+v"(vr));
+    asm volatile("" : "+v"(qc0), "+v"(qc1), "+v"(oc0), "+v"(oc1));
+    f32x16 sv = zero16(), dpv;
+    // dP - D: the accumulator starts at -D of each query row
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 nd = *(const float4*)&sm.dterm[buf][half * 32 + 8 * g + 4 * h];
+      dpv[4 * g] = nd.x;
+      dpv[4 * g + 1] = nd.y;
+      dpv[4 * g + 2] = nd.z;
+      dpv[4 * g + 3] = nd.w;
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) sv = mfma_32x32x16(row_frag(sbase, qr, ks), kf[ks], sv);
+    float nlv[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 l4 = *(const float4*)&sm.lse[buf][half * 32 + 8 * g + 4 * h];
+      nlv[4 * g] = l4.x;
+      nlv[4 * g + 1] = l4.y;
+      nlv[4 * g + 2] = l4.z;
+      nlv[4 * g + 3] = l4.w;
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) dpv = mfma_32x32x16(row_frag(sbase, orow, ks), row_frag(sbase, vr, ks), dpv);
+    u32x4 pb[2], db[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      float pv[8], dv[8];
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int g = 2 * st + g2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          float pp = fast_exp2(__builtin_fmaf(sv[i], c, nlv[i]));
+          if (NM) {
+            const int q = qh0 + 8 * g + 4 * h + e;
+            if (q >= Nq || (MASK == 1 && kj > q + off)) pp = 0.f;
+          }
+          pv[4 * g2 + e] = pp;
+          dv[4 * g2 + e] = pp * dpv[i];
+        }
+      }
+      pb[st] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                     pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+      db[st] = u32x4{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]),
+                     pack_bf16x2(dv[4], dv[5]), pack_bf16x2(dv[6], dv[7])};
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const uint8_t* rowp = sbase + hrow + st * 16 * 2 * D;
+        dvT[dt] = mfma_32x32x16(col_frag(rowp, oc0, oc1, dt), pb[st], dvT[dt]);
+        dkT[dt] = mfma_32x32x16(col_frag(rowp, qc0, qc1, dt), db[st], dkT[dt]);
+      }
+  };
+  // masked: some (query, key) pair of this wave's half-tile is not visible,
+  // or the half-tile reaches past the last query
+  auto needm = [&](int it) {
+    const int qh0 = it * kDkv8Q + 32 * half;
+    return (MASK == 1 && qh0 + off < kw0 + 31) || qh0 + 32 > Nq;
+  };
+  int buf = 0;
+  auto step = [&](auto nm) {
+    int itn = next_in_head(it + 1), jn = j;
+    if (itn >= nqt && j + 1 < G) {   // on to the next query head of the group
+      itn = next_in_head(qbeg);
+      jn = j + 1;
+    }
+    if (itn < nqt) issue(itn, jn, buf ^ 1);
+    tile(buf, it * kDkv8Q, nm);
+    wait_vmem();
+    __syncthreads();
+    buf ^= 1;
+    it = itn;
+    j = jn;
+  };
+
+  wait_vmem();
+  __syncthreads();
+  while (it < nqt) {
+    while (it < nqt && needm(it)) step(std::true_type{});
+    while (it < nqt && !needm(it)) step(std::false_type{});
+  }
+
+  // Sum the two halves' partial accumulators of each key group, dK first,
+  // then dV: the second half writes its fp32 partials to LDS (the tiles are
+  // no longer read: the loop ended with a barrier), the first adds them and
+  // writes the result.
+  float* xch = (float*)&sm;                              // [kg][dt][i][lane]
+  uint16_t* __restrict__ dKrow = (uint16_t*)p.dk + sq.kb + hk * p.k_hs + kj * p.k_rs;
+  uint16_t* __restrict__ dVrow = (uint16_t*)p.dv + sq.kb + hk * p.k_hs + kj * p.k_rs;
+  auto exchange = [&](f32x16 (&acc)[NDT], uint16_t* __restrict__ out, float mul) {
+    __syncthreads();
+    if (half == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[((kg * NDT + dt) * 16 + i) * 64 + lane] = acc[dt][i];
+    }
+    __syncthreads();
+    if (half == 0 && kj < Nk) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        float a[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a[i] = (acc[dt][i] + xch[((kg * NDT + dt) * 16 + i) * 64 + lane]) * mul;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(u32x2*)(out + dt * 32 + 8 * g + 4 * h) =
+              u32x2{pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+      }
+    }
+  };
+  exchange(dkT, dKrow, p.scale);   // dK = scale dS^T Q
+  exchange(dvT, dVrow, 1.0f);
+}
+
+// ---------------------------------------------------------------------------
 // dQ: one workgroup per 128-query tile
 // ---------------------------------------------------------------------------
 constexpr int kDqBQ = 128;   // queries per workgroup
@@ -590,8 +847,11 @@ static int launch_bwd_t(const AttnParams& p, int steps, hipStream_t stream) {
     uint32_t nkt = (uint32_t)((p.Nk + kDkvBK - 1) / kDkvBK);
     uint32_t total = nkt * (uint32_t)p.B * (uint32_t)p.Hkv;
     void* args[] = {&pp, &nkt, &total};
-    hipError_t e = hipLaunchKernel((const void*)&bwd_dkdv_bf16_kernel<D, MASK>, dim3(total), dim3(kThreads),
-                                   args, 0, stream);
+    hipError_t e;
+    if (D == 128 && FA_DKDV8)
+      e = hipLaunchKernel((const void*)&bwd_dkdv8_bf16_kernel<MASK>, dim3(total), dim3(kDkv8Threads), args, 0, stream);
+    else
+      e = hipLaunchKernel((const void*)&bwd_dkdv_bf16_kernel<D, MASK>, dim3(total), dim3(kThreads), args, 0, stream);
     if (e != hipSuccess) return (int)e;
   }
   if (steps & kBwdDq) {
