@@ -215,7 +215,7 @@ def naive_full(q, k, v, do, scale, mask_kind, bool_mask, backward):
 # rocprofv3 summaries (text for profiles/), read from the SQLite output
 # ---------------------------------------------------------------------------
 KEYS_BY_SUBSTR = (("fwd_bf16_kernel", "fwd"), ("bwd_rowterm_bf16_kernel", "rowterm"),
-                  ("bwd_dkdv_bf16_kernel", "dkdv"), ("bwd_dq_bf16_kernel", "dq"),
+                  ("bwd_dkdv_bf16_kernel", "dkdv"), ("bwd_dkdv8_bf16_kernel", "dkdv"), ("bwd_dq_bf16_kernel", "dq"),
                   ("splitkv_bf16_kernel", "splitkv"), ("splitkv_combine_kernel", "combine"),
                   ("fwd_fp8_kernel", "fwd_fp8"))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -543,8 +543,10 @@ def main() -> int:
 
     peak = PEAK_BF16_TFLOPS if w.dtype == synth.DTYPE_BF16 else PEAK_F32_VALU_TFLOPS
     kflop = {"fwd": fwd_flop, "rowterm": 0.0, "dkdv": 8.0 * w.d * vis * heads, "dq": 2.0 * w.d * vis * heads}
-    kname = KERNEL_NAMES if w.dtype == synth.DTYPE_BF16 else {n: KERNEL_NAMES[n].replace("_bf16_", "_f32_")
-                                                              for n in names}
+    kname = dict(KERNEL_NAMES) if w.dtype == synth.DTYPE_BF16 else {n: KERNEL_NAMES[n].replace("_bf16_", "_f32_")
+                                                                    for n in names}
+    if w.dtype == synth.DTYPE_BF16 and w.d == 128:
+        kname["dkdv"] = "bwd_dkdv8_bf16_kernel"     # the eight-wave dK/dV kernel at d = 128
     kernels = {}
     for n in names:
         t = float(per[n].mean())
