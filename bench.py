@@ -430,6 +430,9 @@ def main() -> int:
     ap.add_argument("--summarize-stalls", nargs="+", metavar="DB",
                     help="per-kernel shares of wave cycles (issuing / waiting on a dependency / waiting for issue) "
                          "from the stall counter passes")
+    ap.add_argument("--atomic-rate", action="store_true",
+                    help="fp32 atomic-add throughput (torch index_add_), each address updated 1, 8 or 32 times: "
+                         "the rate an atomic dQ accumulation would run at")
     ap.add_argument("--summarize-counters", metavar="DB",
                     help="per-kernel table (clock, MFMA busy, executed MFMA FLOPs, ...) from a counter pass")
     args = ap.parse_args()
@@ -471,6 +474,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.sweep:
         return run_sweep(args, dev)
+    if args.atomic_rate:
+        return run_atomic_rate(dev)
     if args.tile_sweep:
         return run_tile_sweep(args, dev)
     if args.workload in synth.PACKED_WORKLOADS:
@@ -826,6 +831,39 @@ def run_packed(args, w: synth.PackedWorkload, dev) -> int:
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }
     print(json.dumps(rec), flush=True)
+    return 0
+
+
+def run_atomic_rate(dev) -> int:
+    """Device-wide throughput of fp32 atomic adds (index_add_ with repeated
+    indices: every address receives `adds` updates, as a dQ accumulator
+    would from the key tiles of one query tile). Each update also reads its
+    8-byte index and 4-byte source value. HIP-event medians."""
+    import torch
+    n = 1 << 23                                          # 32 MiB of fp32 accumulators
+    acc = torch.zeros(n, dtype=torch.float32, device=dev)
+    out = []
+    for adds in (1, 8, 32):
+        idx = torch.arange(n, device=dev, dtype=torch.int64).repeat(adds)
+        src = torch.ones(n * adds, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            acc.index_add_(0, idx, src)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for e0, e1 in ev:
+            e0.record()
+            acc.index_add_(0, idx, src)
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+        rec = {"updates_per_address": adds, "ms": round(ms, 4),
+               "atomic_updates_tb_s": round(n * adds * 4 / (ms * 1e-3) / 1e12, 3)}
+        out.append(rec)
+        print(json.dumps(rec), flush=True)
+        del idx, src
+    print("| updates per address | ms | fp32 atomic updates (TB/s) |")
+    print("|---|---|---|")
+    for r in out:
+        print(f"| {r['updates_per_address']} | {r['ms']} | {r['atomic_updates_tb_s']} |")
     return 0
 
 
