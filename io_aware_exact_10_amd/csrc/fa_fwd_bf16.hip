@@ -123,7 +123,7 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   };
   TileLoader<D, kFwdBC, NW> ld;
   ld.init(w, lane, (int)(p.k_rs * 2));
-  auto issue = [&](int kt, int buf) {
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
     ld.load(sm.k[buf], Kh, kt * kFwdBC, Nk);
     ld.load(sm.v[buf], Vh, kt * kFwdBC, Nk);
   };
@@ -183,28 +183,32 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) s1 = mfma_32x32x16(kf[ks], qf[ks], s1);
     }
-    // Scores of a sub-block to the exp2 domain: masked entries -inf.
-    auto scale_mask = [&](f32x16& sv, int kb, bool live) {
+    // Masked entries of a sub-block's scores to -inf; visible scores stay
+    // raw, so they take the same arithmetic as in an unmasked tile (c >= 0:
+    // the scale's sign is folded into Q). Masked entries are kept out of the
+    // products with c explicitly, since c may be 0.
+    auto apply_mask = [&](f32x16& sv, int kb, bool live) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
         const bool vis = live && key < Nk && (MASK != 1 || key <= qi + off);
-        sv[i] = vis ? sv[i] * c : -INFINITY;
+        sv[i] = vis ? sv[i] : -INFINITY;
       }
     };
     float mx0 = -INFINITY, mx1 = -INFINITY;
-    if (NM) scale_mask(s0, 0, true);
+    if (NM) apply_mask(s0, 0, true);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx0 = fmaxf(mx0, s0[i]);
     __builtin_amdgcn_sched_barrier(0);
-    if (NM) scale_mask(s1, 1, live1);
+    if (NM) apply_mask(s1, 1, live1);
     if (live1) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx1 = fmaxf(mx1, s1[i]);
     }
     float mx = fmaxf(mx0, mx1);
     mx = xor32_max(mx);
-    if (!NM) mx *= c;
+    if (NM) mx = mx == -INFINITY ? mx : mx * c;   // c = 0 (zero scale): -inf * 0 would be NaN
+    else mx *= c;
     // Raise the reference max only when some row of the wave outgrows it.
     if (__ballot(mx > m_run + kRescaleThreshold)) {
       const float m_new = fmaxf(m_run, mx);
@@ -228,7 +232,7 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float t = sv[8 * st + e];
-          x[e] = NM ? fast_exp2(t - m_use) : fast_exp2(__builtin_fmaf(t, c, -m_use));
+          x[e] = NM && t == -INFINITY ? 0.f : fast_exp2(__builtin_fmaf(t, c, -m_use));
           l_run += x[e];
         }
         pb[st] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
