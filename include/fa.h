@@ -289,6 +289,18 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* ls
 const char* fa_status_string(int status);
 
 /*
+ * Debugging aid, not part of the method: while on != 0, every kernel launched
+ * by a later call of this library takes its workgroups' work items (query or
+ * key tiles, heads, sequences) in the reverse of the usual order. Each work
+ * item is computed by one workgroup with no atomics and no communication
+ * between workgroups, so results must be bitwise identical in both orders;
+ * a difference points at a race (e.g. an LDS buffer reused too early). The
+ * setting is process-wide and takes effect at the next call. Returns the
+ * previous setting (0 or 1). Never fails.
+ */
+int fa_debug_reverse_order(int on);
+
+/*
  * fa_bwd without a workspace argument, for callers that cannot allocate
  * device memory: code recorded into a HIP graph, tight serving loops,
  * harnesses that forbid hipMalloc. It computes exactly what fa_bwd computes

@@ -31,7 +31,7 @@ __all__ = [
     "FAError", "fa_fwd", "fa_fwd_tiled", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen", "fa_bwd_varlen",
     "fa_bwd_varlen_workspace_bytes", "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
-    "fa_fwd_fp8", "fa_bwd_noalloc", "forward", "backward", "backward_noalloc", "forward_varlen", "backward_varlen", "forward_splitkv", "forward_fp8",
+    "fa_fwd_fp8", "fa_bwd_noalloc", "fa_debug_reverse_order", "forward", "backward", "backward_noalloc", "forward_varlen", "backward_varlen", "forward_splitkv", "forward_fp8",
     "library_path", "lib",
 ]
 
@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_noalloc.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_debug_reverse_order.argtypes = [i]
+        L.fa_debug_reverse_order.restype = i
         _lib = L
     return _lib
 
@@ -119,6 +121,12 @@ def declared_functions() -> list[str]:
 # ---------------------------------------------------------------------------
 def fa_status_string(status: int) -> str:
     return lib().fa_status_string(int(status)).decode()
+
+
+def fa_debug_reverse_order(on: int) -> int:
+    """Debug switch: later launches take their work items in reverse order
+    (results must not change). Returns the previous setting."""
+    return int(lib().fa_debug_reverse_order(int(on)))
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:

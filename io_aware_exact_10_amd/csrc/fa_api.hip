@@ -15,6 +15,10 @@ namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 40;   // per tensor; offsets are 64-bit inside
 
+// Debug switch (fa_debug_reverse_order): launches made while it is set take
+// their workgroups' work items in reverse order.
+std::atomic<int> g_reverse_order{0};
+
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // [a, a+na) and [b, b+nb) overlap?
@@ -50,6 +54,7 @@ fa::AttnParams make_params(int B, int H, int N, int d, float scale, int mask_kin
   p.scale = scale;
   p.c = fabsf(scale) * 1.4426950408889634f;
   p.qflip = scale < 0.f ? 0x80008000u : 0u;
+  p.rev = g_reverse_order.load() ? 1u : 0u;
   p.block_mask = mask_kind == FA_MASK_BLOCK_SPARSE ? block_mask : nullptr;
   fa::set_dense_layout(p);
   return p;
@@ -78,6 +83,10 @@ void set_dense_layout(AttnParams& p) {
 }  // namespace fa
 
 extern "C" {
+
+int fa_debug_reverse_order(int on) {
+  return g_reverse_order.exchange(on ? 1 : 0);
+}
 
 const char* fa_status_string(int status) {
   switch (status) {
@@ -357,6 +366,7 @@ fa::AttnParams varlen_params(const int* cu_q, const int* cu_k, int B, int H, int
   p.scale = scale;
   p.c = fabsf(scale) * 1.4426950408889634f;
   p.qflip = scale < 0.f ? 0x80008000u : 0u;
+  p.rev = g_reverse_order.load() ? 1u : 0u;
   p.Hkv = Hkv;
   p.Nq = max_q;
   p.Nk = max_k;
@@ -577,6 +587,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* ls
   p.scale = scale;
   p.c = fabsf(sk) * 1.4426950408889634f;
   p.qflip = sk < 0.f ? 0x80808080u : 0u;   // E4M3 sign bit of every Q byte
+  p.rev = g_reverse_order.load() ? 1u : 0u;
   p.ldv = ldv;
   p.vscale = v_descale;
   p.q = q;

@@ -116,7 +116,7 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   // exec masks.
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
-  const uint32_t L = xcd_remap(blockIdx.x, total);
+  const uint32_t L = work_item(p.rev, total);
   const uint32_t bh = L / nkt;                 // (K/V head, batch), head-major as in the forward kernel
   const int kt = (int)(L - bh * nkt);
   const int k0 = kt * kDkvBK;
@@ -398,7 +398,7 @@ void bwd_dkdv8_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
   const int kg = w & 3, half = w >> 2;                  // key group, query half
-  const uint32_t L = xcd_remap(blockIdx.x, total);
+  const uint32_t L = work_item(p.rev, total);
   const uint32_t bh = L / nkt;                          // (K/V head, batch), head-major
   const int kt = (int)(L - bh * nkt);
   const int k0 = kt * kDkvBK;
@@ -636,7 +636,7 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   // exec masks.
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
-  const uint32_t L = xcd_remap(blockIdx.x, total);
+  const uint32_t L = work_item(p.rev, total);
   const uint32_t bh = L / nqt;
   uint32_t qt = L - bh * nqt;
   if (MASK == 1) qt = nqt - 1 - qt;

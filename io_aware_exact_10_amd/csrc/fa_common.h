@@ -221,6 +221,14 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t wg, uint32_t total) {
   return x * q + (x < r ? x : r) + s;
 }
 
+// Logical work item of this workgroup: the XCD-aware order, or that order
+// reversed (rev = 1, a debug switch: every workgroup computes the same
+// result in any order, so a difference between the two orders exposes a race).
+__device__ __forceinline__ uint32_t work_item(uint32_t rev, uint32_t total) {
+  const uint32_t L = xcd_remap(blockIdx.x, total);
+  return rev ? total - 1u - L : L;
+}
+
 // Block-sparse mask scanner: finds visible 128-blocks along one row (or one
 // column, with a stride) of the block mask, 64 entries per ballot.
 struct MaskScan {

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(AttnParams p, uint
   __shared__ float vs[kF32BK][D];
   const int N = p.N;
   const int tid = threadIdx.x, sl = tid % G;
-  const uint32_t L = xcd_remap(blockIdx.x, total);
+  const uint32_t L = work_item(p.rev, total);
   const uint32_t bh = L / nqt;
   const int q0 = (int)(L - bh * nqt) * ROWS;
   const int qi = q0 + tid / G;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dkdv_f32_kernel(AttnParams p,
   __shared__ float l2s[kF32BK], dts[kF32BK];
   const int N = p.N;
   const int tid = threadIdx.x, sl = tid % G;
-  const uint32_t L = xcd_remap(blockIdx.x, total);
+  const uint32_t L = work_item(p.rev, total);
   const uint32_t bh = L / nkt;
   const int k0 = (int)(L - bh * nkt) * ROWS;
   const int kj = k0 + tid / G;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dq_f32_kernel(AttnParams p, u
   __shared__ float vs[kF32BK][D];
   const int N = p.N;
   const int tid = threadIdx.x, sl = tid % G;
-  const uint32_t L = xcd_remap(blockIdx.x, total);
+  const uint32_t L = work_item(p.rev, total);
   const uint32_t bh = L / nqt;
   const int q0 = (int)(L - bh * nqt) * ROWS;
   const int qi = q0 + tid / G;

@@ -82,7 +82,7 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
 
-  const uint32_t L = xcd_remap(blockIdx.x, total);
+  const uint32_t L = work_item(p.rev, total);
   const uint32_t bh = L / nqt;
   uint32_t qt = L - bh * nqt;
   if (MASK == 1) qt = nqt - 1 - qt;            // causal: longest rows first

@@ -89,7 +89,7 @@ void fwd_fp8_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   // exec masks.
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
-  const uint32_t L = xcd_remap(blockIdx.x, total);
+  const uint32_t L = work_item(p.rev, total);
   const uint32_t bh = L / nqt;
   uint32_t qt = L - bh * nqt;
   if (MASK == 1) qt = nqt - 1 - qt;     // causal: longest rows first

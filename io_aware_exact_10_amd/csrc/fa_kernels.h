@@ -25,6 +25,7 @@ struct AttnParams {
   float scale;              // as given (any sign)
   float c;                  // |scale| * log2(e): scores -> exp2 domain
   uint32_t qflip;           // 0x80008000 when scale < 0: bf16 sign flip of Q pairs
+  uint32_t rev;             // 1: workgroups take their work items in reverse order (debug switch)
 
   // Shapes and strides of the bf16 kernels. Dense [B, H, N, d]: Hkv = H,
   // Nq = Nk = N, cu_q = cu_k = null. Packed batches: sequence b owns tokens

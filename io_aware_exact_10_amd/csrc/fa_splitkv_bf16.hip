@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64 * NW) void splitkv_bf16_kernel(AttnParams p, uin
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
   const int S = p.splits;
-  const uint32_t L = xcd_remap(blockIdx.x, total);
+  const uint32_t L = work_item(p.rev, total);
   const uint32_t bh = L / (uint32_t)S;
   const int sp = (int)(L - bh * (uint32_t)S);
   const int hk = (int)bh / p.B, bat = (int)bh - hk * p.B;   // head-major, as in the forward kernel

@@ -55,10 +55,19 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"fa_fwd", "fa_fwd_tiled", "fa_bwd", "fa_bwd_rowterm", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_varlen",
                           "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_splitkv_splits",
-                          "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_bwd_noalloc"}
+                          "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_bwd_noalloc",
+                          "fa_debug_reverse_order"}
     L = fa.lib()
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_debug_reverse_order_switch():
+    """The switch is host state only: it returns the previous setting."""
+    assert fa.fa_debug_reverse_order(1) == 0
+    assert fa.fa_debug_reverse_order(7) == 1
+    assert fa.fa_debug_reverse_order(0) == 1
+    assert fa.fa_debug_reverse_order(0) == 0
 
 
 def test_single_hip_runtime_in_process():
