@@ -78,6 +78,9 @@ void fwd_fp8_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   constexpr int kF8BR = 32 * NW;        // queries per workgroup
   __shared__ F8Smem<D> sm;
   constexpr int NDT = D / 32;            // 32-row blocks of O^T
+  // V^T blocks read ahead of the vector work: two (all at d = 64); all four
+  // at d = 128 would not fit the registers. Same-box timings: 0-7 % faster.
+  constexpr int NPRE = NDT < 2 ? NDT : 2;
   constexpr int NKS = D / 64;            // 64-byte contraction steps of S^T
   constexpr int PK = kF8BC * D / 1024;   // 1 KiB pieces per K (and per V^T) tile
   constexpr int PER = PK / kF8NW;        // pieces per wave
@@ -174,6 +177,15 @@ void fwd_fp8_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
         s[kb] = mfma_f8_32x32x64(lds_frag(rp, c0 ^ sw, (c0 + 1) ^ sw), qf[ks], s[kb]);
       }
     }
+    // The V^T fragments of the first NPRE column blocks are read here, ahead
+    // of the vector work, so their LDS latency is hidden behind it.
+    i32x8 vpre[NPRE > 0 ? NPRE : 1];
+#pragma unroll
+    for (int dt = 0; dt < NPRE; ++dt) {
+      const int row = 32 * dt + r;
+      const int sw = f8_swz_v(row);
+      vpre[dt] = lds_frag(sm.v[buf] + row * kF8BC, (2 * h) ^ sw, (2 * h + 1) ^ sw);
+    }
     __builtin_amdgcn_sched_barrier(0);
     float mx = -INFINITY;
 #pragma unroll
@@ -232,7 +244,7 @@ void fwd_fp8_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     for (int dt = 0; dt < NDT; ++dt) {
       const int row = 32 * dt + r;
       const int sw = f8_swz_v(row);
-      i32x8 vf = lds_frag(sm.v[buf] + row * kF8BC, (2 * h) ^ sw, (2 * h + 1) ^ sw);
+      i32x8 vf = dt < NPRE ? vpre[dt < NPRE ? dt : 0] : lds_frag(sm.v[buf] + row * kF8BC, (2 * h) ^ sw, (2 * h + 1) ^ sw);
       if (NM) {
 #pragma unroll
         for (int wd = 0; wd < 8; ++wd) vf[wd] = (int)((uint32_t)vf[wd] & vmask[wd]);
