@@ -185,8 +185,9 @@ def test_backward_steps_match_fa_bwd(mask_kind, dtype):
 
 @pytest.mark.parametrize("mask_kind", [NONE, CAUSAL])
 def test_long_sequence_shape(mask_kind):
-    """From 16K queries the forward runs eight waves per workgroup: a ragged
-    16K+ sequence checked on sampled rows (start, end, random)."""
+    """Long sequences run the eight-wave forward (at d = 128 from 4K queries
+    without a mask, 8K causal): a ragged 16K+ sequence checked on sampled
+    rows (start, end, random)."""
     w = synth.small_workload(1, 2, 16411, 128, BF, mask_kind, seed=3700 + mask_kind, backward=False)
     inp = synth.make_inputs(w)
     t = to_device(inp)
