@@ -64,6 +64,13 @@ struct alignas(16) FwdSmem {
 };
 
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
+// Unmasked tiles: the K fragment reads of a tile's S products run this many
+// reads ahead of the products (the compiler's own order keeps them one ahead).
+// Same-box timings: 0.5-3 % faster than one ahead; two and five ahead measured
+// in between.
+#ifndef FA_FWD_KDIST
+#define FA_FWD_KDIST 3
+#endif
 
 template <int D, int MASK, int NW_, int NBUF>
 __global__ __launch_bounds__((FwdShape<D, MASK, NW_, NBUF>::THREADS))
@@ -176,18 +183,40 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
     // Unmasked tiles are visible to every row, so both sub-blocks are live.
     const bool live1 = !NM || !(MASK == 1 && k0 + 32 > qw0 + 31 + off);
 
-    u32x4 kf[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) kf[ks] = row_frag(sbase, kbase, ks);
     f32x16 s0 = zero16(), s1 = zero16();
+    if (!NM && FA_FWD_KDIST > 0) {
+      // Unmasked: K fragment reads run KDIST ahead of the products.
+      constexpr int KS = D / 16, KD = FA_FWD_KDIST;
+      u32x4 ka[KS], kb2[KS];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) s0 = mfma_32x32x16(kf[ks], qf[ks], s0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (live1) {
+      for (int ks = 0; ks < KS; ++ks) ka[ks] = row_frag(sbase, kbase, ks);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) kf[ks] = row_frag(sbase + 32 * 2 * D, kbase, ks);
+      for (int ks = 0; ks < KS; ++ks) kb2[ks] = row_frag(sbase + 32 * 2 * D, kbase, ks);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) s1 = mfma_32x32x16(kf[ks], qf[ks], s1);
+      for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16(ka[ks], qf[ks], s0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s1 = mfma_32x32x16(kb2[ks], qf[ks], s1);
+      __builtin_amdgcn_sched_group_barrier(0x100, KD, 0);
+#pragma unroll
+      for (int j = 0; j < 2 * KS - KD; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KD, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      u32x4 kf[D / 16];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) kf[ks] = row_frag(sbase, kbase, ks);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) s0 = mfma_32x32x16(kf[ks], qf[ks], s0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (live1) {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) kf[ks] = row_frag(sbase + 32 * 2 * D, kbase, ks);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) s1 = mfma_32x32x16(kf[ks], qf[ks], s1);
+      }
     }
     // The V^T fragments of the first NPRE column blocks of a sub-block are
     // read ahead (vpre), so their LDS latency hides behind the vector work.
