@@ -48,9 +48,11 @@
  *   `stream` (asynchronous); FA_ERR_HIP means a launch failed (the HIP error
  *   is not cleared). A device fault surfaces at the caller's next
  *   synchronisation.
- * State. No global mutable state (fa_bwd_noalloc aside: it uses one
- *   library-owned scratch array per GPU); calls are thread-safe. Results
- *   are bitwise deterministic from run to run (no atomics).
+ * State. No global mutable state besides fa_bwd_noalloc's library-owned
+ *   scratch array per GPU and the debug switch fa_debug_reverse_order (an
+ *   atomic flag read when a call builds its launch); calls are thread-safe.
+ *   Results are bitwise deterministic from run to run (no atomics), and do
+ *   not depend on the debug switch.
  */
 #ifndef FA_H_
 #define FA_H_
