@@ -37,6 +37,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -109,9 +110,15 @@ def visible_pairs(w: synth.Workload, mask: np.ndarray | None) -> int:
 
 
 def source_digest(*files: str) -> str:
+    """Digest of the kernel sources with comments and blank space removed,
+    so that a counter record stays valid across comment-only edits and goes
+    stale on any change of the code itself."""
     h = hashlib.sha256()
     for f in files:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        src = open(os.path.join(ROOT, f)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

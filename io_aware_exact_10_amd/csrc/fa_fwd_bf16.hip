@@ -28,6 +28,10 @@
 //   O^T += V^T P^T  B = P^T straight from the S^T registers (rounded to
 //                   bf16), A = V^T read from the row-major V tile with LDS
 //                   transpose reads, in the key order P^T occupies.
+// The loops wait on LDS latency (about 40-50 cycles per read) rather than on
+// LDS bandwidth, so operand reads are issued early: the K reads of the S
+// products run three ahead of them, and the first V^T blocks of each P.V
+// product are read before the exponentials it waits for.
 // Epilogue: O = acc / l, LSE = ln 2 * (m + log2 l).
 #include <type_traits>
 
