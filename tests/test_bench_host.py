@@ -144,3 +144,13 @@ def test_visible_pairs_of_a_row_sample_match_oracle_mask(mask_kind):
     rows = np.arange(0, N, 7)
     vis = oracle.visible(rows, N, mask_kind, inp.mask)
     assert bench.visible_pairs_rows(w, inp.mask, rows) == int(vis.sum())
+
+
+def test_source_digest_ignores_comments_only(tmp_path):
+    """A counter record stays valid across comment edits and goes stale on code edits."""
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text("// header\nint f(int x) { return x + 1; }  /* note */\n")
+    b.write_text("// another header\n/* block\n comment */\nint f(int x) {\n  return x + 1;  // tail\n}\n")
+    c.write_text("// header\nint f(int x) { return x + 2; }\n")
+    assert bench.source_digest(str(a)) == bench.source_digest(str(b))
+    assert bench.source_digest(str(a)) != bench.source_digest(str(c))
