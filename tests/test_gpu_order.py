@@ -21,15 +21,15 @@ NONE, CAUSAL, BSP = synth.MASK_NONE, synth.MASK_CAUSAL, synth.MASK_BLOCK_SPARSE
 
 def both_orders(fn):
     """fn() -> tuple of tensors, run in the usual and the reversed order."""
-    assert fa.fa_debug_reverse_order(0) == 0
-    a = [x.clone() for x in fn()]
-    torch.cuda.synchronize()
-    fa.fa_debug_reverse_order(1)
+    prev = fa.fa_debug_reverse_order(0)
     try:
+        a = [x.clone() for x in fn()]
+        torch.cuda.synchronize()
+        fa.fa_debug_reverse_order(1)
         b = [x.clone() for x in fn()]
         torch.cuda.synchronize()
     finally:
-        fa.fa_debug_reverse_order(0)
+        fa.fa_debug_reverse_order(prev)
     return a, b
 
 
