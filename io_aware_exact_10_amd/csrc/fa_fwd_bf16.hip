@@ -78,7 +78,7 @@ constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 template <int D, int MASK, int NW_, int NBUF>
 __global__ __launch_bounds__((FwdShape<D, MASK, NW_, NBUF>::THREADS))
-__attribute__((amdgpu_waves_per_eu(D == 128 || NW_ == 8 ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu(D == 128 || NW_ == 8 ? 2 : (MASK != 1 ? 4 : 3))))
 void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   __shared__ FwdSmem<D, NBUF> sm;
   constexpr int NW = NW_;
@@ -86,11 +86,14 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   constexpr int TPB = kMaskBlock / kFwdBC;                 // key tiles per mask block
   constexpr int NDT = D / 32;                              // 32-row blocks of O^T
   // V^T column blocks of a sub-block read ahead of its P.V products: half of
-  // them at d = 128 (all would not fit the registers), all at d = 64 except
-  // in the eight-wave shape, whose 128-register budget keeps two workgroups
-  // per CU. Same-box timings: d = 128 forward 2-12 % faster, d = 64 four-wave
-  // 1-2 %, d = 64 eight-wave 12 % slower with any read-ahead.
-  constexpr int NPRE = D == 128 ? NDT / 2 : (NW_ == 8 ? 0 : NDT);
+  // them at d = 128 (all would not fit the registers); at d = 64 all of them
+  // in the causal four-wave shape only. The other d = 64 shapes keep a
+  // 128-register budget instead: four waves per SIMD (two eight-wave or four
+  // four-wave workgroups per CU) hide more latency than the read-ahead does.
+  // Same-box timings: d = 128 forward 2-12 % faster with the read-ahead; at
+  // d = 64 without a mask or with a block mask, four waves per SIMD are 5-6 %
+  // faster than three with the read-ahead, causal 7 % slower (it spills).
+  constexpr int NPRE = D == 128 ? NDT / 2 : (NW_ == 8 || MASK != 1 ? 0 : NDT);
 
   // The wave index is the same in every lane; reading it into a scalar makes
   // everything derived from it (row ranges, tile classes, loop bounds, LDS
@@ -366,20 +369,26 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   }
 
   // Epilogue: combine the two lane halves' partial sums, normalise, store.
+  // At d = 64 the lane index is taken afresh here, so that no lane-derived
+  // address is held across the tile loops (at 128 registers it would be
+  // spilled to scratch memory); at d = 128 that choice makes the register
+  // allocation spill elsewhere, so the index from the prologue is kept.
+  const int lane_e = D == 64 ? (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) : lane;
+  const int he = lane_e >> 5, qe = qw0 + (lane_e & 31);
   const float lt = xor32_sum(l_run);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (qi < Nq) {
-    uint16_t* __restrict__ Orow = (uint16_t*)p.o + sq.qb + hq * p.q_hs + qi * q_rs;
+  if (qe < Nq) {
+    uint16_t* __restrict__ Orow = (uint16_t*)p.o + sq.qb + hq * p.q_hs + qe * q_rs;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int dd = dt * 32 + 8 * g + 4 * h;
+        const int dd = dt * 32 + 8 * g + 4 * he;
         u32x2 val = {pack_bf16x2(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv),
                      pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
         *(u32x2*)(Orow + dd) = val;
       }
-    if (h == 0) p.lse[sq.lb + hq * p.l_hs + qi] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+    if (he == 0) p.lse[sq.lb + hq * p.l_hs + qe] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
