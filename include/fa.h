@@ -126,7 +126,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   dV = P^T dO; dP = dO V^T; D = rowsum(dO * O); dS = P * (dP - D);
  *   dQ = scale dS K; dK = scale dS^T Q.
  * Three kernels run in order on `stream`: the row term, then dK/dV (one
- * workgroup per key tile), then dQ (one workgroup per query tile).
+ * workgroup per key tile), then dQ (one workgroup per query tile); under a
+ * causal mask a workgroup takes a pair of tiles whose work adds up evenly.
  * workspace: caller-owned device memory of at least
  * fa_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte aligned; its contents
  * on entry are ignored and on exit are unspecified.
@@ -294,8 +295,9 @@ const char* fa_status_string(int status);
  * Debugging aid, not part of the method: while on != 0, every kernel launched
  * by a later call of this library takes its workgroups' work items (query or
  * key tiles, heads, sequences) in the reverse of the usual order. Each work
- * item is computed by one workgroup with no atomics and no communication
- * between workgroups, so results must be bitwise identical in both orders;
+ * item (a tile, or a causal pair of tiles) is computed by one workgroup with
+ * no atomics and no communication between workgroups, so results must be
+ * bitwise identical in both orders;
  * a difference points at a race (e.g. an LDS buffer reused too early). The
  * setting is process-wide and takes effect at the next call. Returns the
  * previous setting (0 or 1). Never fails.

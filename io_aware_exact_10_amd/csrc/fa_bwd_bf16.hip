@@ -37,7 +37,9 @@
 // index of the *accumulated* output (a key for dK/dV, a query for dQ) on the
 // lane, which lets P and dS feed the next product as B operands directly.
 // Both loop kernels double-buffer their LDS tiles: tile t+1 is copied while
-// tile t is computed.
+// tile t is computed. Under a causal mask each workgroup of either kernel
+// takes two tiles of one sequence and head, j and n - 1 - j, one after the
+// other, so every workgroup does the same work (causal_pair_tile).
 #include <type_traits>
 
 #include "fa_common.h"
@@ -122,15 +124,30 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   // everything derived from it (row ranges, tile classes, loop bounds, LDS
   // copy destinations) scalar, so the tile loops branch on scalars instead of
   // exec masks.
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, r = lane & 31;
+  const int lane0 = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Work items: one key tile of one (batch, K/V head), or under a causal mask
+  // the pair of key tiles j and nks - 1 - j of one sequence and head, whose
+  // visible query ranges add up to the same length (causal_pair_tile).
+  constexpr int kItems = MASK == 1 ? 2 : 1;
   const uint32_t L = work_item(p.rev, total);
-  const uint32_t bh = L / nkt;                 // (K/V head, batch), head-major as in the forward kernel
-  const int kt = (int)(L - bh * nkt);
-  const int k0 = kt * kDkvBK;
+  const uint32_t npair = MASK == 1 ? (nkt + 1) / 2 : nkt;   // workgroups per (batch, K/V head)
+  const uint32_t bh = L / npair, pj = L - bh * npair;      // (K/V head, batch), head-major as in the forward kernel
   const int hk = (int)bh / p.B, bat = (int)bh - hk * p.B;
   const SeqView sq = seq_view(p, bat);
-  if (k0 >= sq.nk) return;                     // past this sequence's keys (packed batches)
+  const int nks = (sq.nk + kDkvBK - 1) / kDkvBK;
+  for (int item = 0; item < kItems; ++item) {
+  const int kt = MASK == 1 ? causal_pair_tile(pj, item, nks, false) : (int)pj;
+  if (MASK == 1 && kt < 0) break;
+  const int k0 = kt * kDkvBK;
+  if (k0 >= sq.nk) break;                      // past this sequence's keys (packed batches)
+  // Lane index behind an opaque copy per item (causal pairs): lane-derived
+  // values are not hoisted out of the item loop and held across both items.
+  int lane = lane0;
+  if (kItems > 1) {
+    lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+  }
+  const int h = lane >> 5, r = lane & 31;
   const int Nq = sq.nq, Nk = sq.nk;
   const int off = Nk - Nq;                     // causal: key j visible to query i iff j <= i + off
   const int G = p.H / p.Hkv;                   // query heads sharing this K/V head
@@ -384,6 +401,7 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
         *(u32x2*)(dVrow + dd) = b;
       }
   }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -421,16 +439,27 @@ void bwd_dkdv8_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   constexpr int QPB = kMaskBlk / kDkv8Q;               // query tiles per mask block
   __shared__ Dkv8Smem sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, r = lane & 31;
+  const int lane0 = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kg = w & 3, half = w >> 2;                  // key group, query half
+  // Work items as in the four-wave kernel: one key tile, or a causal pair.
+  constexpr int kItems = MASK == 1 ? 2 : 1;
   const uint32_t L = work_item(p.rev, total);
-  const uint32_t bh = L / nkt;                          // (K/V head, batch), head-major
-  const int kt = (int)(L - bh * nkt);
-  const int k0 = kt * kDkvBK;
+  const uint32_t npair = MASK == 1 ? (nkt + 1) / 2 : nkt;   // workgroups per (batch, K/V head)
+  const uint32_t bh = L / npair, pj = L - bh * npair;      // (K/V head, batch), head-major
   const int hk = (int)bh / p.B, bat = (int)bh - hk * p.B;
   const SeqView sq = seq_view(p, bat);
-  if (k0 >= sq.nk) return;
+  const int nks = (sq.nk + kDkvBK - 1) / kDkvBK;
+  for (int item = 0; item < kItems; ++item) {
+  const int kt = MASK == 1 ? causal_pair_tile(pj, item, nks, false) : (int)pj;
+  if (MASK == 1 && kt < 0) break;
+  const int k0 = kt * kDkvBK;
+  if (k0 >= sq.nk) break;
+  int lane = lane0;
+  if (kItems > 1) {
+    lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+  }
+  const int h = lane >> 5, r = lane & 31;
   const int Nq = sq.nq, Nk = sq.nk;
   const int off = Nk - Nq;
   const int G = p.H / p.Hkv;
@@ -636,6 +665,10 @@ void bwd_dkdv8_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   };
   exchange(dkT, dKrow, p.scale);   // dK = scale dS^T Q
   exchange(dvT, dVrow, 1.0f);
+  // The next item's copies overwrite the exchange area: wait until every
+  // wave has read its partials.
+  if (kItems > 1) __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -666,19 +699,32 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   // everything derived from it (row ranges, tile classes, loop bounds, LDS
   // copy destinations) scalar, so the tile loops branch on scalars instead of
   // exec masks.
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, r = lane & 31;
+  const int lane0 = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Work items as in the forward kernel: one query tile of one (batch, head),
+  // or under a causal mask the pair of query tiles j and nqs - 1 - j.
+  constexpr int kItems = MASK == 1 ? 2 : 1;
   const uint32_t L = work_item(p.rev, total);
-  const uint32_t bh = L / nqt;
-  uint32_t qt = L - bh * nqt;
-  if (MASK == 1) qt = nqt - 1 - qt;
-  const int q0 = (int)qt * kDqBQ;
+  const uint32_t npair = MASK == 1 ? (nqt + 1) / 2 : nqt;   // workgroups per (batch, head)
+  const uint32_t bh = L / npair, pj = L - bh * npair;
   const int hq = (int)bh / p.B, bat = (int)bh - hq * p.B;   // head-major, as in the forward kernel
   const SeqView sq = seq_view(p, bat);
-  if (q0 >= sq.nq) return;                     // past this sequence's queries (packed batches)
+  const int nqs = (sq.nq + kDqBQ - 1) / kDqBQ;
+  for (int item = 0; item < kItems; ++item) {
+  const int qt = MASK == 1 ? causal_pair_tile(pj, item, nqs, true) : (int)pj;
+  if (MASK == 1 && qt < 0) break;
+  const int q0 = qt * kDqBQ;
+  if (q0 >= sq.nq) break;                      // past this sequence's queries (packed batches)
+  // Lane index behind an opaque copy per item (causal pairs): lane-derived
+  // values are not hoisted out of the item loop and held across both items.
+  int lane = lane0;
+  if (kItems > 1) {
+    lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+  }
+  const int h = lane >> 5, r = lane & 31;
   const int Nq = sq.nq, Nk = sq.nk;
   const int off = Nk - Nq;                     // causal: key j visible to query i iff j <= i + off
-  const int hk = hq / (p.H / p.Hkv);
+  const int hk = kItems > 1 ? __builtin_amdgcn_readfirstlane(hq / (p.H / p.Hkv)) : hq / (p.H / p.Hkv);
   const int qw0 = q0 + 32 * w;
   const int qi = qw0 + r;
   const int64_t q_rs = p.q_rs;
@@ -873,6 +919,7 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
         *(u32x2*)(dQrow + dd) = a;
       }
   }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -891,7 +938,7 @@ static int launch_bwd_t(const AttnParams& p, int steps, hipStream_t stream) {
   }
   if (steps & kBwdDkdv) {
     uint32_t nkt = (uint32_t)((p.Nk + kDkvBK - 1) / kDkvBK);
-    uint32_t total = nkt * (uint32_t)p.B * (uint32_t)p.Hkv;
+    uint32_t total = (MASK == 1 ? (nkt + 1) / 2 : nkt) * (uint32_t)p.B * (uint32_t)p.Hkv;
     void* args[] = {&pp, &nkt, &total};
     hipError_t e;
     if (D == 128 && FA_DKDV8)
@@ -902,7 +949,7 @@ static int launch_bwd_t(const AttnParams& p, int steps, hipStream_t stream) {
   }
   if (steps & kBwdDq) {
     uint32_t nqt = (uint32_t)((p.Nq + kDqBQ - 1) / kDqBQ);
-    uint32_t total = nqt * (uint32_t)p.B * (uint32_t)p.H;
+    uint32_t total = (MASK == 1 ? (nqt + 1) / 2 : nqt) * (uint32_t)p.B * (uint32_t)p.H;
     void* args[] = {&pp, &nqt, &total};
     hipError_t e = hipLaunchKernel((const void*)&bwd_dq_bf16_kernel<D, MASK>, dim3(total), dim3(kThreads),
                                    args, 0, stream);

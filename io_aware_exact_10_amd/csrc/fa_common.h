@@ -229,6 +229,20 @@ __device__ __forceinline__ uint32_t work_item(uint32_t rev, uint32_t total) {
   return rev ? total - 1u - L : L;
 }
 
+// Causal work pairs. Under a causal mask the work of a tile grows (query
+// tiles) or shrinks (key tiles) linearly along the sequence, so tiles j and
+// n - 1 - j of one sequence and head together cost about the same for every
+// j. A workgroup takes pair j: item 0 is the longer tile (the higher index
+// when long_high, else the lower), item 1 the shorter. Returns the tile
+// index, or -1 where the pair has no such item (j past the pairs of an n-tile
+// sequence, or the middle tile of an odd n, which has no partner).
+__device__ __forceinline__ int causal_pair_tile(uint32_t j, int item, int n, bool long_high) {
+  if ((int)j >= (n + 1) / 2) return -1;
+  const int lo = (int)j, hi = n - 1 - (int)j;
+  if (item == 1 && lo == hi) return -1;
+  return (item == 0) == long_high ? hi : lo;
+}
+
 // Block-sparse mask scanner: finds visible 128-blocks along one row (or one
 // column, with a stride) of the block mask, 64 entries per ballot.
 struct MaskScan {

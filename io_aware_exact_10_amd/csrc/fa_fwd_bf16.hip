@@ -6,11 +6,12 @@
 // online softmax, tiling and fusion, one log-sum-exp per row). Only O and the
 // row log-sum-exp are written; the N x N scores stay in registers.
 //
-// Work decomposition: one workgroup per (query tile, batch, head); each wave
-// owns 32 query rows (4 waves, 128 rows, or 8 waves, 256 rows, for long
-// sequences; 32 and 64 rows on request), and query tiles run
-// in parallel over the sequence ("Core ideas": parallelism over the sequence
-// dimension). The workgroup streams 64-key tiles of K and V through LDS,
+// Work decomposition: one workgroup per (query tile, batch, head), or with a
+// causal mask per pair of query tiles of one (batch, head) whose visible key
+// ranges add up to the same length; each wave owns 32 query rows (4 waves,
+// 128 rows, or 8 waves, 256 rows, for long sequences; 32 and 64 rows on
+// request), and query tiles run in parallel over the sequence ("Core ideas":
+// parallelism over the sequence dimension). The workgroup streams 64-key tiles of K and V through LDS,
 // double-buffered: tile t+1 is copied global -> LDS asynchronously (no
 // registers) while tile t is computed.
 //
@@ -99,23 +100,39 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   // everything derived from it (row ranges, tile classes, loop bounds, LDS
   // copy destinations) scalar, so the tile loops branch on scalars instead of
   // exec masks.
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, r = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const uint32_t L = work_item(p.rev, total);
-  const uint32_t bh = L / nqt;
-  uint32_t qt = L - bh * nqt;
-  if (MASK == 1) qt = nqt - 1 - qt;            // causal: longest rows first
-  const int q0 = (int)qt * kFwdBR;
-  // Head-major: each XCD's contiguous share of the grid covers whole heads
-  // of every sequence, so ragged packed batches spread evenly over the XCDs
-  // and the query heads of one K/V group share an L2.
+  // Work items: one query tile of one (batch, head). Causal: a workgroup
+  // takes two, query tiles j and nqs - 1 - j of one sequence and head
+  // (nqs = that sequence's query tiles), longest first, so every workgroup
+  // sees about nqs + 1 key tiles and no short tiles are left for the end of
+  // the grid (causal_pair_tile). Otherwise one item per workgroup.
+  // Head-major order: each XCD's contiguous share of the grid covers whole
+  // heads of every sequence, so ragged packed batches spread evenly over the
+  // XCDs and the query heads of one K/V group share an L2.
+  constexpr int kItems = MASK == 1 ? 2 : 1;
+  const uint32_t G = work_item(p.rev, total);
+  const uint32_t npair = MASK == 1 ? (nqt + 1) / 2 : nqt;   // workgroups per (batch, head)
+  const uint32_t bh = G / npair, j = G - bh * npair;
   const int hq = (int)bh / p.B, bat = (int)bh - hq * p.B;
   const SeqView sq = seq_view(p, bat);
-  if (q0 >= sq.nq) return;                     // past this sequence's queries (packed batches)
+  const uint32_t nqs = (uint32_t)((sq.nq + kFwdBR - 1) / kFwdBR);
+  for (int it = 0; it < kItems; ++it) {
+  const int qt = MASK == 1 ? causal_pair_tile(j, it, (int)nqs, true) : (int)j;
+  if (qt < 0) break;
+  const int q0 = qt * kFwdBR;
+  if (q0 >= sq.nq) break;                      // past this sequence's queries (packed batches)
+  // The lane index is taken per item behind an opaque copy, so lane-derived
+  // values are not hoisted out of the item loop and held across both items.
+  // (Not in the one-wave shape, which has registers to spare: there the copy
+  // leads the compiler to an invalid comparison against the LDS aperture.)
+  int lane = threadIdx.x & 63;
+  if (NW > 1) asm volatile("" : "+v"(lane));
+  const int h = lane >> 5, r = lane & 31;
   const int Nq = sq.nq, Nk = sq.nk;
   const int off = Nk - Nq;                     // causal: key j visible to query i iff j <= i + off
-  const int hk = hq / (p.H / p.Hkv);
+  // Uniform quotient, read into a scalar so the K/V head pointers stay scalar.
+  const int hk = __builtin_amdgcn_readfirstlane(hq / (p.H / p.Hkv));
   const uint16_t* __restrict__ Qh = (const uint16_t*)p.q + sq.qb + hq * p.q_hs;
   const uint16_t* __restrict__ Kh = (const uint16_t*)p.k + sq.kb + hk * p.k_hs;
   const uint16_t* __restrict__ Vh = (const uint16_t*)p.v + sq.kb + hk * p.k_hs;
@@ -369,11 +386,11 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   }
 
   // Epilogue: combine the two lane halves' partial sums, normalise, store.
-  // At d = 64 the lane index is taken afresh here, so that no lane-derived
-  // address is held across the tile loops (at 128 registers it would be
-  // spilled to scratch memory); at d = 128 that choice makes the register
-  // allocation spill elsewhere, so the index from the prologue is kept.
-  const int lane_e = D == 64 ? (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) : lane;
+  // Where registers are tightest the lane index is taken afresh here, so
+  // that no lane-derived address is held across the tile loops (it would be
+  // spilled to scratch memory); in the other shapes that choice makes the
+  // register allocation spill elsewhere, so the item's index is kept.
+  const int lane_e = D == 64 || (MASK == 1 && NW == 8) ? (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) : lane;
   const int he = lane_e >> 5, qe = qw0 + (lane_e & 31);
   const float lt = xor32_sum(l_run);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -389,6 +406,7 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
         *(u32x2*)(Orow + dd) = val;
       }
     if (he == 0) p.lse[sq.lb + hq * p.l_hs + qe] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+  }
   }
 }
 
@@ -414,7 +432,8 @@ template <int D, int MASK, int NW, int NBUF>
 static int launch_fwd_s(const AttnParams& p, hipStream_t stream) {
   using S = FwdShape<D, MASK, NW, NBUF>;
   const uint32_t nqt = (uint32_t)((p.Nq + S::BR - 1) / S::BR);
-  const uint32_t total = nqt * (uint32_t)p.B * (uint32_t)p.H;
+  const uint32_t per_bh = MASK == 1 ? (nqt + 1) / 2 : nqt;   // workgroups per (batch, head)
+  const uint32_t total = per_bh * (uint32_t)p.B * (uint32_t)p.H;
   AttnParams pp = p;
   void* args[] = {&pp, (void*)&nqt, (void*)&total};
   return (int)hipLaunchKernel((const void*)&fwd_bf16_kernel<D, MASK, NW, NBUF>, dim3(total), dim3(S::THREADS),
