@@ -114,7 +114,7 @@ struct alignas(16) DkvSmem {
 // resident, so it runs one wave per SIMD; d = 64 fits two.
 template <int D, int MASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2)))
-void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
+void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total, uint32_t pairs) {
   __shared__ DkvSmem<D> sm;
   constexpr int NDT = D / 32;
   constexpr int NPRE = D == 64 ? kDkvPre : 0;
@@ -130,13 +130,14 @@ void bwd_dkdv_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   // visible query ranges add up to the same length (causal_pair_tile).
   constexpr int kItems = MASK == 1 ? 2 : 1;
   const uint32_t L = work_item(p.rev, total);
-  const uint32_t npair = MASK == 1 ? (nkt + 1) / 2 : nkt;   // workgroups per (batch, K/V head)
+  const bool paired = MASK == 1 && pairs != 0;
+  const uint32_t npair = paired ? (nkt + 1) / 2 : nkt;   // workgroups per (batch, K/V head)
   const uint32_t bh = L / npair, pj = L - bh * npair;      // (K/V head, batch), head-major as in the forward kernel
   const int hk = (int)bh / p.B, bat = (int)bh - hk * p.B;
   const SeqView sq = seq_view(p, bat);
   const int nks = (sq.nk + kDkvBK - 1) / kDkvBK;
   for (int item = 0; item < kItems; ++item) {
-  const int kt = MASK == 1 ? causal_pair_tile(pj, item, nks, false) : (int)pj;
+  const int kt = paired ? causal_pair_tile(pj, item, nks, false) : (item == 0 ? (int)pj : -1);
   if (MASK == 1 && kt < 0) break;
   const int k0 = kt * kDkvBK;
   if (k0 >= sq.nk) break;                      // past this sequence's keys (packed batches)
@@ -433,7 +434,7 @@ static_assert(4 * 4 * 16 * 64 * sizeof(float) <= 2 * kDkvBK * 128 * 2, "exchange
 
 template <int MASK>
 __global__ __launch_bounds__(kDkv8Threads) __attribute__((amdgpu_waves_per_eu(2)))
-void bwd_dkdv8_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
+void bwd_dkdv8_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total, uint32_t pairs) {
   constexpr int D = 128;
   constexpr int NDT = D / 32;
   constexpr int QPB = kMaskBlk / kDkv8Q;               // query tiles per mask block
@@ -444,13 +445,14 @@ void bwd_dkdv8_bf16_kernel(AttnParams p, uint32_t nkt, uint32_t total) {
   // Work items as in the four-wave kernel: one key tile, or a causal pair.
   constexpr int kItems = MASK == 1 ? 2 : 1;
   const uint32_t L = work_item(p.rev, total);
-  const uint32_t npair = MASK == 1 ? (nkt + 1) / 2 : nkt;   // workgroups per (batch, K/V head)
+  const bool paired = MASK == 1 && pairs != 0;
+  const uint32_t npair = paired ? (nkt + 1) / 2 : nkt;   // workgroups per (batch, K/V head)
   const uint32_t bh = L / npair, pj = L - bh * npair;      // (K/V head, batch), head-major
   const int hk = (int)bh / p.B, bat = (int)bh - hk * p.B;
   const SeqView sq = seq_view(p, bat);
   const int nks = (sq.nk + kDkvBK - 1) / kDkvBK;
   for (int item = 0; item < kItems; ++item) {
-  const int kt = MASK == 1 ? causal_pair_tile(pj, item, nks, false) : (int)pj;
+  const int kt = paired ? causal_pair_tile(pj, item, nks, false) : (item == 0 ? (int)pj : -1);
   if (MASK == 1 && kt < 0) break;
   const int k0 = kt * kDkvBK;
   if (k0 >= sq.nk) break;
@@ -689,7 +691,7 @@ struct alignas(16) DqSmem {
 template <int D, int MASK>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 128 ? (MASK == 2 ? 1 : 2) : 3)))
-void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
+void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total, uint32_t pairs) {
   __shared__ DqSmem<D> sm;
   constexpr int NDT = D / 32;
   constexpr int NPRE = kDqPre;
@@ -704,14 +706,18 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
   // or under a causal mask the pair of query tiles j and nqs - 1 - j.
   constexpr int kItems = MASK == 1 ? 2 : 1;
   const uint32_t L = work_item(p.rev, total);
-  const uint32_t npair = MASK == 1 ? (nqt + 1) / 2 : nqt;   // workgroups per (batch, head)
+  const bool paired = MASK == 1 && pairs != 0;
+  const uint32_t npair = paired ? (nqt + 1) / 2 : nqt;   // workgroups per (batch, head)
   const uint32_t bh = L / npair, pj = L - bh * npair;
   const int hq = (int)bh / p.B, bat = (int)bh - hq * p.B;   // head-major, as in the forward kernel
   const SeqView sq = seq_view(p, bat);
   const int nqs = (sq.nq + kDqBQ - 1) / kDqBQ;
   for (int item = 0; item < kItems; ++item) {
-  const int qt = MASK == 1 ? causal_pair_tile(pj, item, nqs, true) : (int)pj;
-  if (MASK == 1 && qt < 0) break;
+  int qt = (int)pj;
+  if (MASK == 1) {
+    qt = paired ? causal_pair_tile(pj, item, nqs, true) : (item == 0 ? (int)(nqt - 1 - pj) : -1);
+    if (qt < 0) break;
+  }
   const int q0 = qt * kDqBQ;
   if (q0 >= sq.nq) break;                      // past this sequence's queries (packed batches)
   // Lane index behind an opaque copy per item (causal pairs): lane-derived
@@ -928,6 +934,8 @@ void bwd_dq_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total) {
 template <int D, int MASK>
 static int launch_bwd_t(const AttnParams& p, int steps, hipStream_t stream) {
   AttnParams pp = p;
+  // Causal pairs for dense batches only, as in the forward launcher.
+  uint32_t pairs = MASK == 1 && p.cu_q == nullptr ? 1u : 0u;
   if (steps & kBwdRowterm) {
     const size_t threads = (size_t)p.rt_rows * (D / 8);
     const uint32_t grid = (uint32_t)((threads + kThreads - 1) / kThreads);
@@ -938,8 +946,8 @@ static int launch_bwd_t(const AttnParams& p, int steps, hipStream_t stream) {
   }
   if (steps & kBwdDkdv) {
     uint32_t nkt = (uint32_t)((p.Nk + kDkvBK - 1) / kDkvBK);
-    uint32_t total = (MASK == 1 ? (nkt + 1) / 2 : nkt) * (uint32_t)p.B * (uint32_t)p.Hkv;
-    void* args[] = {&pp, &nkt, &total};
+    uint32_t total = (pairs ? (nkt + 1) / 2 : nkt) * (uint32_t)p.B * (uint32_t)p.Hkv;
+    void* args[] = {&pp, &nkt, &total, &pairs};
     hipError_t e;
     if (D == 128 && FA_DKDV8)
       e = hipLaunchKernel((const void*)&bwd_dkdv8_bf16_kernel<MASK>, dim3(total), dim3(kDkv8Threads), args, 0, stream);
@@ -949,8 +957,8 @@ static int launch_bwd_t(const AttnParams& p, int steps, hipStream_t stream) {
   }
   if (steps & kBwdDq) {
     uint32_t nqt = (uint32_t)((p.Nq + kDqBQ - 1) / kDqBQ);
-    uint32_t total = (MASK == 1 ? (nqt + 1) / 2 : nqt) * (uint32_t)p.B * (uint32_t)p.H;
-    void* args[] = {&pp, &nqt, &total};
+    uint32_t total = (pairs ? (nqt + 1) / 2 : nqt) * (uint32_t)p.B * (uint32_t)p.H;
+    void* args[] = {&pp, &nqt, &total, &pairs};
     hipError_t e = hipLaunchKernel((const void*)&bwd_dq_bf16_kernel<D, MASK>, dim3(total), dim3(kThreads),
                                    args, 0, stream);
     if (e != hipSuccess) return (int)e;
