@@ -127,7 +127,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   dQ = scale dS K; dK = scale dS^T Q.
  * Three kernels run in order on `stream`: the row term, then dK/dV (one
  * workgroup per key tile), then dQ (one workgroup per query tile); under a
- * causal mask a workgroup takes a pair of tiles whose work adds up evenly.
+ * causal mask over a dense batch a workgroup takes a pair of tiles whose
+ * work adds up evenly.
  * workspace: caller-owned device memory of at least
  * fa_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte aligned; its contents
  * on entry are ignored and on exit are unspecified.

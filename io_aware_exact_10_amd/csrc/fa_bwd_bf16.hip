@@ -37,9 +37,10 @@
 // index of the *accumulated* output (a key for dK/dV, a query for dQ) on the
 // lane, which lets P and dS feed the next product as B operands directly.
 // Both loop kernels double-buffer their LDS tiles: tile t+1 is copied while
-// tile t is computed. Under a causal mask each workgroup of either kernel
-// takes two tiles of one sequence and head, j and n - 1 - j, one after the
-// other, so every workgroup does the same work (causal_pair_tile).
+// tile t is computed. Under a causal mask over a dense batch each workgroup
+// of either kernel takes two tiles of one sequence and head, j and n - 1 - j,
+// one after the other, so every workgroup does the same work
+// (causal_pair_tile).
 #include <type_traits>
 
 #include "fa_common.h"

@@ -7,11 +7,12 @@
 // row log-sum-exp are written; the N x N scores stay in registers.
 //
 // Work decomposition: one workgroup per (query tile, batch, head), or with a
-// causal mask per pair of query tiles of one (batch, head) whose visible key
-// ranges add up to the same length; each wave owns 32 query rows (4 waves,
-// 128 rows, or 8 waves, 256 rows, for long sequences; 32 and 64 rows on
-// request), and query tiles run in parallel over the sequence ("Core ideas":
-// parallelism over the sequence dimension). The workgroup streams 64-key tiles of K and V through LDS,
+// causal mask over a dense batch per pair of query tiles of one (batch, head)
+// whose visible key ranges add up to the same length; each wave owns 32
+// query rows (4 waves, 128 rows, or 8 waves, 256 rows, for long sequences;
+// 32 and 64 rows on request), and query tiles run in parallel over the
+// sequence ("Core ideas": parallelism over the sequence dimension). The
+// workgroup streams 64-key tiles of K and V through LDS,
 // double-buffered: tile t+1 is copied global -> LDS asynchronously (no
 // registers) while tile t is computed.
 //
