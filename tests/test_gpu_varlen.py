@@ -125,7 +125,10 @@ def test_decode_shaped_queries():
 @pytest.mark.parametrize("mask_kind", [NONE, CAUSAL])
 def test_packed_equal_lengths_bitwise_equals_dense(mask_kind, d):
     """Equal lengths and Hkv = H: the packed call runs the same arithmetic as
-    fa_fwd / fa_bwd on the [B, H, N, d] transpose, so results are bitwise equal."""
+    fa_fwd / fa_bwd on the [B, H, N, d] transpose, so results are bitwise equal.
+    Under a causal mask the dense call gives each workgroup a pair of tiles
+    (j, n - 1 - j) and the packed call one tile, so this also checks the two
+    schedules against each other (N = 333: three tiles, one without a partner)."""
     B, H, N = 3, 4, 333
     p = synth.packed_inputs([N] * B, [N] * B, H, H, d, seed=5300 + d + mask_kind)
     got = run_varlen(p, mask_kind)
