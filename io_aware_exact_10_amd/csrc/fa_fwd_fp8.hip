@@ -41,9 +41,13 @@ __device__ __forceinline__ f32x16 mfma_f8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// Four floats -> four E4M3 codes in order (round to nearest even).
+// Four floats -> four E4M3 codes in order (round to nearest even). The first
+// conversion writes the low half of the word and keeps the high half of its
+// "old" operand, which the second conversion then overwrites, so any value
+// serves as that operand: a's own bits let the compiler convert in place
+// instead of first zeroing a register.
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
