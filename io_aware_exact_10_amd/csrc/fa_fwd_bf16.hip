@@ -418,7 +418,8 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total, uint32_t pairs)
 
 // Query length from which the eight-wave (256-row) shape is used, from
 // interleaved timings of both shapes at B * N = 32K tokens, H = 16:
-//   causal, d = 128: from 8K (1-2 % faster at 8K, 2-4 % from 16K; 5 % slower at 4K);
+//   causal, d = 128: from 8K (1-2 % faster at 8K, 2-4 % from 16K; 5 % slower at 4K
+//   with one tile per workgroup, within +-3 % at 4K with causal work pairs);
 //   causal, d = 64: never (5-10 % slower at 32K);
 //   no mask, d = 128: from 4K (2 % at 4K, 5-6 % from 8K); no mask, d = 64: from 2K (4-6 %).
 #ifndef FA_FWD_LONG_N
