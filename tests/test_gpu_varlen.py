@@ -146,6 +146,34 @@ def test_packed_equal_lengths_bitwise_equals_dense(mask_kind, d):
         assert np.array_equal(got[n], back(x)), n
 
 
+# Random dense shapes (seeded): B, H in 1..4, N in 1..700, d in {64, 128}.
+_PAIR_SHAPES = [(int(b), int(h), int(n), int(d)) for b, h, n, d in zip(
+    np.random.default_rng(71).integers(1, 5, 12), np.random.default_rng(72).integers(1, 5, 12),
+    np.random.default_rng(73).integers(1, 701, 12), np.random.default_rng(74).choice([64, 128], 12))]
+
+
+@pytest.mark.parametrize("B,H,N,d", _PAIR_SHAPES)
+def test_causal_pairs_bitwise_equal_single_tiles(B, H, N, d):
+    """Causal work pairs (dense call: a workgroup takes query or key tiles j
+    and n - 1 - j) against one tile per workgroup (packed call of the same
+    equal-length sequences): the per-tile arithmetic is the same, so O, LSE
+    and all gradients must agree bit for bit at any tile count, odd or even."""
+    p = synth.packed_inputs([N] * B, [N] * B, H, H, d, seed=7100 + N)
+    got = run_varlen(p, CAUSAL)
+    t = to_dev(p)
+    dense = lambda x: x.view(B, N, H, d).permute(0, 2, 1, 3).contiguous()
+    announce(f"dense pairs B{B} H{H} N{N} d{d}")
+    q, k, v, do = (dense(t[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, None, CAUSAL)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, None, CAUSAL)
+    torch.cuda.synchronize()
+    back = lambda x: x.permute(0, 2, 1, 3).reshape(B * N, H, d).float().cpu().numpy()
+    assert np.array_equal(got["o"], back(o))
+    assert np.array_equal(got["lse"], lse.permute(1, 0, 2).reshape(H, B * N).cpu().numpy())
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.array_equal(got[n], back(x)), n
+
+
 def test_rows_outside_every_sequence_are_untouched():
     """Tokens past the last offset keep what the caller stored there."""
     p = synth.packed_inputs([70, 0, 150], [90, 33, 150], 4, 2, 64, seed=5400, pad_q=37, pad_k=21)
