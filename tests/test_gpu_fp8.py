@@ -219,3 +219,18 @@ def test_fp8_long_sequence_shape(mask_kind):
         O, L = oracle.forward_head(f.q[0, h], f.k[0, h], f.v[0, h], 1.0 / math.sqrt(d), mask_kind, rows=rows)
         check_random((o[0, h][rows], lse[0, h][rows]), (O, L), f.q[0, h], f.k[0, h], f.v[0, h], mask_kind,
                      1.0 / math.sqrt(d), f"long head {h}", rows=rows)
+
+
+def test_fp8_causal_pairs_and_single_tiles_agree_on_shared_rows():
+    """Causal rows depend only on the keys up to their own position, so a
+    causal sequence of N = 16384 queries (128 query tiles: paired, each
+    workgroup takes tiles j and 127 - j) must give bit for bit the first
+    16384 rows of the same inputs extended to 16512 queries (129 tiles: one
+    tile per workgroup, longest first)."""
+    B, H, d, N1, N2 = 1, 2, 128, 16384, 16512
+    f = synth.fp8_inputs(B, H, N2, d, seed=8600)
+    o2, l2 = run_fp8(f, CAUSAL, 1.0 / math.sqrt(d))
+    # the same V^T rows (ldv = N2 >= N1) and the first N1 rows of Q and K
+    o1, l1 = run_fp8(f, CAUSAL, 1.0 / math.sqrt(d), q8=f.q8[:, :, :N1], k8=f.k8[:, :, :N1])
+    assert np.array_equal(o1, o2[:, :, :N1])
+    assert np.array_equal(l1, l2[:, :, :N1])
