@@ -293,6 +293,32 @@ def summarize_counters(db_path: str, substrs=("fa::",)) -> str:
     return "\n".join(lines)
 
 
+def summarize_pmc(db_path: str, substrs=("fa::",)) -> str:
+    """Per-kernel means over dispatches of every counter a rocprofv3 --pmc
+    pass collected (derived counters such as LdsUtil included), one column per
+    counter in the order first seen."""
+    import collections
+    import sqlite3
+    cur = sqlite3.connect(db_path).cursor()
+    vals = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    names = []
+    for name, did, cn, v in cur.execute(
+            "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+        vals[name][cn][did] += v
+        if cn not in names:
+            names.append(cn)
+    lines = ["| kernel | dispatches | " + " | ".join(names) + " |", "|" + "---|" * (2 + len(names))]
+    for name in sorted(vals):
+        if not any(s in name for s in substrs):
+            continue
+        c = {cn: (sum(d.values()) / len(d), len(d)) for cn, d in vals[name].items()}
+        nd = max(n for _, n in c.values())
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {nd} | "
+                     + " | ".join(f"{c[cn][0]:.4g}" if cn in c else "nan" for cn in names) + " |")
+    return "\n".join(lines)
+
+
 def summarize_traffic(fetch_db: str, write_db: str, workload: str, copy_bytes: int, update: bool) -> str:
     """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for a copy of copy_bytes."""
@@ -442,11 +468,16 @@ def main() -> int:
                          "the rate an atomic dQ accumulation would run at")
     ap.add_argument("--summarize-counters", metavar="DB",
                     help="per-kernel table (clock, MFMA busy, executed MFMA FLOPs, ...) from a counter pass")
+    ap.add_argument("--summarize-pmc", metavar="DB",
+                    help="per-kernel means of every counter in a rocprofv3 --pmc pass (e.g. LdsUtil, LdsLatency)")
     args = ap.parse_args()
 
     if args.summarize_step_traffic:
         f_db, w_db, steps = args.summarize_step_traffic
         print(summarize_step_traffic(f_db, w_db, args.copy_bytes, int(steps)))
+        return 0
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
         return 0
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))

@@ -97,6 +97,22 @@ def test_stall_summary_shares(tmp_path):
     assert cells[7:9] == ["5.50", "1.50"]
 
 
+def test_pmc_summary_means_every_counter(tmp_path):
+    """Per-kernel means over dispatches of each counter in the pass; kernels
+    outside the library are left out."""
+    db = str(tmp_path / "l.db")
+    k = "void fa::bwd_dkdv8_bf16_kernel<1>(fa::AttnParams, unsigned int, unsigned int, unsigned int)"
+    _db(db, [(k, 1, "LdsUtil", 30.0, 1.0), (k, 2, "LdsUtil", 36.0, 1.0),
+             (k, 1, "LdsLatency", 40.0, 1.0), (k, 2, "LdsLatency", 50.0, 1.0),
+             ("void other_kernel(int)", 3, "LdsUtil", 99.0, 1.0)])
+    out = bench.summarize_pmc(db).splitlines()
+    assert out[0] == "| kernel | dispatches | LdsUtil | LdsLatency |"
+    rows = [l for l in out[2:]]
+    assert len(rows) == 1
+    cells = [c.strip() for c in rows[0].split("|")]
+    assert cells[1:5] == ["`fa::bwd_dkdv8_bf16_kernel<1>`", "2", "33", "45"]
+
+
 def test_hbm_rate():
     assert bench.hbm_rate(None, 1.0) is None
     assert bench.hbm_rate(8e9, 1.0) == 8000.0            # 8 GB in 1 ms
