@@ -395,7 +395,9 @@ void fwd_bf16_kernel(AttnParams p, uint32_t nqt, uint32_t total, uint32_t pairs)
   // Where registers are tightest the lane index is taken afresh here, so
   // that no lane-derived address is held across the tile loops (it would be
   // spilled to scratch memory); in the other shapes that choice makes the
-  // register allocation spill elsewhere, so the item's index is kept.
+  // register allocation spill elsewhere, so the item's index is kept. (mbcnt
+  // counts the active lanes below this one: every lane is active here, all
+  // control flow before this point being uniform across the wave.)
   const int lane_e = D == 64 || (MASK == 1 && NW == 8) ? (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) : lane;
   const int he = lane_e >> 5, qe = qw0 + (lane_e & 31);
   const float lt = xor32_sum(l_run);
